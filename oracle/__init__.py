@@ -1,0 +1,201 @@
+"""CPU oracle for block-scaled int8 quantization and the W4A8 grouped GEMM.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg are the only callers.  The product library
+never imports, links or runs anything from this package.
+
+The arithmetic lives in ``oracle_w4a8.c`` (plain C, one IEEE operation at a
+time); this module only compiles it (``build()``), loads it with ctypes and
+marshals numpy arrays.  bf16 tensors are passed as ``np.uint16`` bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle_w4a8.c")
+_LIB = os.path.join(_HERE, "liboracle_w4a8.so")
+
+K_MAX = 150976
+
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile liboracle_w4a8.so with gcc (no fused multiply-add, no fast-math)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+           "-fopenmp", "-shared", "-fPIC", "-Wall", "-Wextra",
+           "-o", _LIB + ".tmp", _SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I32 = ctypes.c_int32
+    sigs = {
+        "oracle_quantize_act_blockwise": [P, I64, I64, I32, P, P],
+        "oracle_dequantize_act_blockwise": [P, P, I64, I64, I32, P, P],
+        "oracle_weight_level1": [P, I64, I64, P, P],
+        "oracle_weight_level2": [P, I64, I64, I32, P, P],
+        "oracle_quantize_w4_grouped": [P, I64, I64, I32, P, P, P],
+        "oracle_dequantize_w4_grouped": [P, P, P, I64, I64, I32, P],
+        "oracle_group_sums": [P, P, I64, I64, I64, I32, P],
+        "oracle_w4a8_gemm": [P, P, P, P, P, I64, I64, I64, I32, P, P],
+        "oracle_w4a8_gemm_bf16act": [P, P, P, P, I64, I64, I64, I32, P, P, P, P],
+        "oracle_num_threads": [],
+    }
+    for name, args in sigs.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError(f"{name}: invalid arguments (rc={rc})")
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def quantize_act_blockwise(x_bf16: np.ndarray, block: int):
+    """bf16 bits [rows, cols] -> (q int8 [rows, cols], scales f32 [rows, cols/block])."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, cols = x.shape
+    if block <= 0 or cols % block:
+        raise ValueError("cols must be a multiple of block")
+    q = np.empty((rows, cols), np.int8)
+    s = np.empty((rows, cols // block), np.float32)
+    _check(_load().oracle_quantize_act_blockwise(_ptr(x), rows, cols, block, _ptr(q), _ptr(s)),
+           "quantize_act_blockwise")
+    return q, s
+
+
+def dequantize_act_blockwise(q: np.ndarray, scales: np.ndarray, block: int):
+    """-> (x_hat f32 [rows, cols], x_hat bf16 bits [rows, cols])."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s = np.ascontiguousarray(scales, dtype=np.float32)
+    rows, cols = q.shape
+    f = np.empty((rows, cols), np.float32)
+    b = np.empty((rows, cols), np.uint16)
+    _check(_load().oracle_dequantize_act_blockwise(_ptr(q), _ptr(s), rows, cols, block,
+                                                   _ptr(f), _ptr(b)),
+           "dequantize_act_blockwise")
+    return f, b
+
+
+def weight_level1(w_bf16: np.ndarray):
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    n, k = w.shape
+    w8 = np.empty((n, k), np.int8)
+    s_ch = np.empty((n,), np.float32)
+    _check(_load().oracle_weight_level1(_ptr(w), n, k, _ptr(w8), _ptr(s_ch)), "weight_level1")
+    return w8, s_ch
+
+
+def weight_level2(w8: np.ndarray, group: int = 64):
+    w8 = np.ascontiguousarray(w8, dtype=np.int8)
+    n, k = w8.shape
+    q = np.empty((n, k), np.int8)
+    s_g = np.empty((n, k // group), np.uint8)
+    _check(_load().oracle_weight_level2(_ptr(w8), n, k, group, _ptr(q), _ptr(s_g)),
+           "weight_level2")
+    return q, s_g
+
+
+def quantize_w4_grouped(w_bf16: np.ndarray, group: int = 64):
+    """bf16 bits [n, k] -> (q int8 [n,k] in [-7,7], s_g uint8 [n,k/group], s_ch f32 [n])."""
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    n, k = w.shape
+    if group <= 0 or k % group:
+        raise ValueError("k must be a multiple of group")
+    q = np.empty((n, k), np.int8)
+    s_g = np.empty((n, k // group), np.uint8)
+    s_ch = np.empty((n,), np.float32)
+    _check(_load().oracle_quantize_w4_grouped(_ptr(w), n, k, group, _ptr(q), _ptr(s_g),
+                                              _ptr(s_ch)),
+           "quantize_w4_grouped")
+    return q, s_g, s_ch
+
+
+def dequantize_w4_grouped(q, s_g, s_ch, group: int = 64):
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s_g = np.ascontiguousarray(s_g, dtype=np.uint8)
+    s_ch = np.ascontiguousarray(s_ch, dtype=np.float32)
+    n, k = q.shape
+    out = np.empty((n, k), np.float64)
+    _check(_load().oracle_dequantize_w4_grouped(_ptr(q), _ptr(s_g), _ptr(s_ch), n, k, group,
+                                                _ptr(out)),
+           "dequantize_w4_grouped")
+    return out
+
+
+def group_sums(a_q, q, group: int = 64):
+    a_q = np.ascontiguousarray(a_q, dtype=np.int8)
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    m, k = a_q.shape
+    n = q.shape[0]
+    P = np.empty((m, n, k // group), np.int32)
+    _check(_load().oracle_group_sums(_ptr(a_q), _ptr(q), m, n, k, group, _ptr(P)),
+           "group_sums")
+    return P
+
+
+def w4a8_gemm(a_q, a_scale, q, s_g, s_ch, group: int = 64, want_y: bool = True):
+    """-> (acc int32 [m,n], y f64 [m,n] or None)."""
+    a_q = np.ascontiguousarray(a_q, dtype=np.int8)
+    a_scale = np.ascontiguousarray(a_scale, dtype=np.float32).reshape(-1)
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s_g = np.ascontiguousarray(s_g, dtype=np.uint8)
+    s_ch = np.ascontiguousarray(s_ch, dtype=np.float32)
+    m, k = a_q.shape
+    n = q.shape[0]
+    acc = np.empty((m, n), np.int32)
+    y = np.empty((m, n), np.float64) if want_y else None
+    _check(_load().oracle_w4a8_gemm(_ptr(a_q), _ptr(a_scale), _ptr(q), _ptr(s_g), _ptr(s_ch),
+                                    m, n, k, group, _ptr(acc), _ptr(y)),
+           "w4a8_gemm")
+    return acc, y
+
+
+def w4a8_gemm_bf16act(a_bf16, q, s_g, s_ch, group: int = 64, want_y: bool = True):
+    """-> (a_q, a_scale, acc, y): per-token quantization (block = k) then the GEMM."""
+    a = np.ascontiguousarray(a_bf16, dtype=np.uint16)
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s_g = np.ascontiguousarray(s_g, dtype=np.uint8)
+    s_ch = np.ascontiguousarray(s_ch, dtype=np.float32)
+    m, k = a.shape
+    n = q.shape[0]
+    a_q = np.empty((m, k), np.int8)
+    a_s = np.empty((m,), np.float32)
+    acc = np.empty((m, n), np.int32)
+    y = np.empty((m, n), np.float64) if want_y else None
+    _check(_load().oracle_w4a8_gemm_bf16act(_ptr(a), _ptr(q), _ptr(s_g), _ptr(s_ch), m, n, k,
+                                            group, _ptr(a_q), _ptr(a_s), _ptr(acc), _ptr(y)),
+           "w4a8_gemm_bf16act")
+    return a_q, a_s, acc, y
