@@ -1,0 +1,192 @@
+/*
+ * w4a8.h -- C ABI of libw4a8.so: block-scaled int8 activation quantization
+ * and a W4A8 grouped GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * Method (pages cited by title and section):
+ *   - Activations: block-wise symmetric int8 with one binary32 scale per block
+ *     taken from the block's absolute maximum, computed in two phases (scales,
+ *     then scaled data), dequantized back to binary32.
+ *     ["EQuARX" verdict page, pith.science arXiv 2506.17615,
+ *      pith_extraction.key_machinery]
+ *   - Weights: two levels -- an INT8 first level per output channel with a
+ *     protective range, then 4-bit codes with a small integer scale per group
+ *     of 64 along K, so that rebuilding the int8 operand is one multiply-add
+ *     and one XOR per four weights.
+ *     ["LiquidGEMM" verdict page, pith.science arXiv 2509.01229,
+ *      referee_report.summary, pith_extraction.key_machinery,
+ *      referee_report.major_comments[2] (paper section 4, Eq. 7),
+ *      skeptic_critique.concrete_test (group size 64)]
+ *   - GEMM: int8 x int8 products accumulated exactly in int32, the integer
+ *     group scale applied per K-group (folded into the int8 weight operand),
+ *     then out = acc * a_scale[m] * ch_scale[n] in binary32.
+ *     ["LiquidGEMM" verdict page, referee_report.summary: INT8 MMA into
+ *      INT32 after in-kernel dequantization]
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are DEVICE pointers into caller-owned memory.  The library
+ *     never allocates or frees device memory and keeps no global state; it is
+ *     safe to call from several host threads.
+ *   - Tensors are row-major and contiguous; bf16 is passed as its 16-bit
+ *     pattern (uint16_t).
+ *   - Every pointer must be 16-byte aligned (W4A8_ERR_MISALIGNED otherwise).
+ *   - Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *     without synchronizing.
+ *   - Argument errors are detected before anything is launched; then nothing
+ *     is written and a non-zero status is returned.  A failed launch returns
+ *     W4A8_ERR_HIP.  Faults during execution surface at the caller's next
+ *     synchronization.  With the environment variable W4A8_DEBUG=1 every
+ *     call synchronizes its stream and reports execution errors as
+ *     W4A8_ERR_HIP.
+ *   - Empty inputs (rows == 0, m == 0, n == 0) are valid and do nothing.
+ *   - NaN or infinite inputs are outside the contract (results unspecified).
+ */
+#ifndef W4A8_H
+#define W4A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A8_ABI_VERSION 1
+#define W4A8_PACK_LAYOUT_V1 1
+/* Weight group size along K (the only supported value). */
+#define W4A8_GROUP 64
+/* Output channels are packed in tiles of 16; n must be a multiple of it. */
+#define W4A8_N_TILE 16
+/* Largest K for which |acc| <= K * 127 * 112 fits in int32. */
+#define W4A8_K_MAX 150976
+/* Weight codes: level-1 protective range and level-2 code range. */
+#define W4A8_W8_RANGE 112
+#define W4A8_W4_RANGE 7
+
+typedef enum {
+    W4A8_OK = 0,
+    W4A8_ERR_NULL = 1,        /* a required pointer is NULL */
+    W4A8_ERR_SHAPE = 2,       /* negative size or a divisibility rule is broken */
+    W4A8_ERR_UNSUPPORTED = 3, /* valid request this build does not implement */
+    W4A8_ERR_MISALIGNED = 4,  /* a pointer is not 16-byte aligned */
+    W4A8_ERR_HIP = 5          /* the HIP runtime reported an error */
+} w4a8_status;
+
+typedef enum {
+    W4A8_F32 = 0,  /* binary32 output */
+    W4A8_BF16 = 1, /* bf16 output: round-to-nearest-even of the binary32 value */
+    W4A8_I32 = 2   /* raw int32 accumulator acc[m,n] (GEMM only; exact) */
+} w4a8_dtype;
+
+/* W4A8_ABI_VERSION of the loaded library. */
+int32_t w4a8_abi_version(void);
+
+/* W4A8_PACK_LAYOUT_V1: version of the packed weight layout this library writes and reads. */
+int32_t w4a8_pack_layout_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *w4a8_status_string(w4a8_status status);
+
+/*
+ * Block-wise int8 quantization of activations ("EQuARX" verdict page,
+ * pith_extraction.key_machinery: absmax per block, one binary32 scale per
+ * block, scale then round).
+ *   x      [rows, cols] bf16 (input)
+ *   q      [rows, cols] int8 (output), codes in [-127, 127]
+ *   scales [rows, cols/block] binary32 (output)
+ * Per block of `block` contiguous elements of a row:
+ *   amax = max |x|,  s = amax / 127,  inv = (amax > 0) ? 127 / amax : 0,
+ *   q = clamp(round_half_even(x * inv), -127, 127) with x * inv one binary32
+ *   multiply; a NaN product (0 * inf when 127/amax overflows) gives 0.
+ * Requires block > 0, block % 8 == 0 and cols % block == 0 (W4A8_ERR_SHAPE).
+ * block == cols gives one scale per row (per token).
+ */
+w4a8_status quantize_act_blockwise(const uint16_t *x, int64_t rows, int64_t cols, int32_t block,
+                                   int8_t *q, float *scales, hipStream_t stream);
+
+/*
+ * Dequantization back to binary32 ("EQuARX" verdict page,
+ * pith_extraction.key_machinery: dequantize to FP32).
+ *   out[r, c] = q[r, c] * scales[r, c / block]   (one binary32 multiply)
+ * out_dtype W4A8_F32 writes float [rows, cols]; W4A8_BF16 writes the bf16
+ * rounding (nearest-even) of that value as uint16_t [rows, cols].
+ * W4A8_I32 is W4A8_ERR_UNSUPPORTED.  Shape rules as for quantize_act_blockwise.
+ */
+w4a8_status dequantize_act_blockwise(const int8_t *q, const float *scales, int64_t rows,
+                                     int64_t cols, int32_t block, void *out,
+                                     w4a8_dtype out_dtype, hipStream_t stream);
+
+/*
+ * Two-level 4-bit weight quantization and packing ("LiquidGEMM" verdict
+ * page, referee_report.summary: INT8 first level, then 4-bit with an integer
+ * group scale; referee_report.major_comments[2]: the group scale is at most 16).
+ *   w         [n, k] bf16, nn.Linear layout (output channel major) (input)
+ *   w_packed  n * k / 2 bytes, packed layout V1 (output, opaque)
+ *   grp_scale n * k / 64 bytes, uint8 group scales in kernel order (output)
+ *   ch_scale  [n] binary32 per-channel scales (output)
+ * Per channel: c = max |w|, ch_scale = c / 112,
+ *   W8 = clamp(round_half_even(w * (112 / c)), -112, 112)  (0 when c == 0).
+ * Per group of 64 along k: m = max |W8|, s_g = max(1, ceil(m / 7)) in [1, 16],
+ *   q = round_half_even(W8 / s_g) in [-7, 7] (exact rational rounding),
+ *   stored as the nibble q + 8.
+ * The effective weight is ch_scale[n] * s_g[n, g] * q[n, k].
+ * Requires group == 64 (else W4A8_ERR_UNSUPPORTED), n % 16 == 0 and
+ * k % 64 == 0 (else W4A8_ERR_SHAPE).  This step is run once per weight.
+ */
+w4a8_status pack_w4_grouped(const uint16_t *w, int64_t n, int64_t k, int32_t group,
+                            uint8_t *w_packed, uint8_t *grp_scale, float *ch_scale,
+                            hipStream_t stream);
+
+/*
+ * Inverse of the packing (test hook): decodes layout V1 back to canonical
+ * codes q [n, k] int8 in [-7, 7] and group scales s_g [n, k / 64] uint8 in
+ * plain row-major order.  Shape rules as for pack_w4_grouped.
+ */
+w4a8_status unpack_w4_grouped(const uint8_t *w_packed, const uint8_t *grp_scale, int64_t n,
+                              int64_t k, int32_t group, int8_t *q, uint8_t *s_g,
+                              hipStream_t stream);
+
+/*
+ * W4A8 GEMM with per-token activation scales.
+ *   a_q       [m, k] int8 activation codes
+ *   a_scale   [m] binary32 per-row activation scales
+ *   w_packed, grp_scale, ch_scale: as written by pack_w4_grouped for [n, k]
+ *   out       [m, n]: W4A8_F32 float, W4A8_BF16 uint16_t, W4A8_I32 int32_t
+ * acc[m, n] = sum_g s_g[n, g] * sum_{k in g} a_q[m, k] * q[n, k]   (int32, exact)
+ * out[m, n] = (float(acc) * a_scale[m]) * ch_scale[n]              (binary32),
+ *             rounded to bf16 (nearest-even) for W4A8_BF16; W4A8_I32 stores acc.
+ * Requires group == 64, n % 16 == 0, k % 64 == 0 and k <= W4A8_K_MAX
+ * (larger k is W4A8_ERR_UNSUPPORTED).  k == 0 writes zeros.
+ */
+w4a8_status w4a8_gemm(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
+                      const uint8_t *grp_scale, const float *ch_scale, int64_t m, int64_t n,
+                      int64_t k, int32_t group, void *out, w4a8_dtype out_dtype,
+                      hipStream_t stream);
+
+/*
+ * Bytes of workspace w4a8_gemm_bf16act needs for m rows of k activations:
+ * the int8 codes [m, k] at offset 0, then the binary32 per-row scales [m] at
+ * offset round_up(m * k, 256).
+ */
+size_t w4a8_gemm_bf16act_workspace_bytes(int64_t m, int64_t k);
+
+/*
+ * Fused entry point from bf16 activations: per-token quantization
+ * (quantize_act_blockwise with block == k) into `workspace`, then w4a8_gemm.
+ * The result equals those two calls bit for bit; the workspace holds the
+ * activation codes and scales afterwards (layout above).  ws_bytes must be
+ * at least w4a8_gemm_bf16act_workspace_bytes(m, k) (W4A8_ERR_SHAPE).
+ * Requires k > 0 and the w4a8_gemm shape rules.
+ */
+w4a8_status w4a8_gemm_bf16act(const uint16_t *a, const uint8_t *w_packed,
+                              const uint8_t *grp_scale, const float *ch_scale, int64_t m,
+                              int64_t n, int64_t k, int32_t group, void *out,
+                              w4a8_dtype out_dtype, void *workspace, size_t ws_bytes,
+                              hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A8_H */

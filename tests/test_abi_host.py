@@ -1,0 +1,148 @@
+"""Host-side checks of libw4a8.so: it loads, exports every function include/w4a8.h
+declares, and rejects invalid arguments before launching anything.
+
+No GPU work happens here: every call below fails validation (or is an empty
+no-op) before the library touches the HIP runtime's launch path; fake pointers
+are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a8.h")
+LIB = os.path.join(ROOT, "w4a8_quantized_gemm_quantize_amd", "libw4a8.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP = range(6)
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libw4a8.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    L = ctypes.CDLL(LIB)
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    L.quantize_act_blockwise.argtypes = [P, I64, I64, I32, P, P, P]
+    L.dequantize_act_blockwise.argtypes = [P, P, I64, I64, I32, P, ctypes.c_int, P]
+    L.pack_w4_grouped.argtypes = [P, I64, I64, I32, P, P, P, P]
+    L.unpack_w4_grouped.argtypes = [P, P, I64, I64, I32, P, P, P]
+    L.w4a8_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I32, P, ctypes.c_int, P]
+    L.w4a8_gemm_bf16act.argtypes = [P, P, P, P, I64, I64, I64, I32, P, ctypes.c_int, P,
+                                    ctypes.c_size_t, P]
+    L.w4a8_gemm_bf16act_workspace_bytes.argtypes = [I64, I64]
+    L.w4a8_gemm_bf16act_workspace_bytes.restype = ctypes.c_size_t
+    L.w4a8_status_string.restype = ctypes.c_char_p
+    return L
+
+
+A = ctypes.c_void_p(0x10000)       # aligned fake device pointers: never dereferenced
+B = ctypes.c_void_p(0x20000)
+C = ctypes.c_void_p(0x30000)
+D = ctypes.c_void_p(0x40000)
+E = ctypes.c_void_p(0x50000)
+MIS = ctypes.c_void_p(0x10008)     # 8-byte aligned only
+NUL = None
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ["quantize_act_blockwise", "dequantize_act_blockwise", "pack_w4_grouped",
+                 "unpack_w4_grouped", "w4a8_gemm", "w4a8_gemm_bf16act",
+                 "w4a8_gemm_bf16act_workspace_bytes", "w4a8_abi_version",
+                 "w4a8_pack_layout_version", "w4a8_status_string"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+
+
+def test_versions_and_status_strings(lib):
+    assert lib.w4a8_abi_version() == 1
+    assert lib.w4a8_pack_layout_version() == 1
+    seen = set()
+    for s in range(6):
+        txt = lib.w4a8_status_string(s).decode()
+        assert txt and txt not in seen
+        seen.add(txt)
+    assert lib.w4a8_status_string(99)
+
+
+def test_quantize_validation(lib):
+    q = lib.quantize_act_blockwise
+    assert q(A, -1, 64, 32, B, C, NUL) == ERR_SHAPE
+    assert q(A, 4, 64, 12, B, C, NUL) == ERR_SHAPE        # block not a multiple of 8
+    assert q(A, 4, 64, 0, B, C, NUL) == ERR_SHAPE
+    assert q(A, 4, 96, 64, B, C, NUL) == ERR_SHAPE        # cols not a multiple of block
+    assert q(NUL, 4, 64, 32, B, C, NUL) == ERR_NULL
+    assert q(A, 4, 64, 32, NUL, C, NUL) == ERR_NULL
+    assert q(A, 4, 64, 32, B, NUL, NUL) == ERR_NULL
+    assert q(MIS, 4, 64, 32, B, C, NUL) == ERR_MISALIGNED
+    assert q(A, 4, 64, 32, B, MIS, NUL) == ERR_MISALIGNED
+    assert q(NUL, 0, 64, 32, NUL, NUL, NUL) == OK          # empty: nothing to do
+
+
+def test_dequantize_validation(lib):
+    d = lib.dequantize_act_blockwise
+    assert d(A, B, 4, 64, 32, C, 2, NUL) == ERR_UNSUPPORTED   # int32 output not defined
+    assert d(A, B, 4, 64, 24, C, 0, NUL) == ERR_SHAPE
+    assert d(A, NUL, 4, 64, 32, C, 0, NUL) == ERR_NULL
+    assert d(A, B, 4, 64, 32, MIS, 1, NUL) == ERR_MISALIGNED
+    assert d(NUL, NUL, 0, 64, 32, NUL, 0, NUL) == OK
+
+
+def test_pack_validation(lib):
+    p = lib.pack_w4_grouped
+    assert p(A, 32, 256, 128, B, C, D, NUL) == ERR_UNSUPPORTED   # group 128
+    assert p(A, 17, 256, 64, B, C, D, NUL) == ERR_SHAPE          # n not a multiple of 16
+    assert p(A, 32, 96, 64, B, C, D, NUL) == ERR_SHAPE           # k not a multiple of 64
+    assert p(A, 32, 256, 64, NUL, C, D, NUL) == ERR_NULL
+    assert p(A, 32, 256, 64, B, C, MIS, NUL) == ERR_MISALIGNED
+    assert p(NUL, 0, 256, 64, NUL, NUL, NUL, NUL) == OK
+    u = lib.unpack_w4_grouped
+    assert u(A, B, 32, 256, 32, C, D, NUL) == ERR_UNSUPPORTED
+    assert u(A, B, 32, 256, 64, NUL, D, NUL) == ERR_NULL
+
+
+def test_gemm_validation(lib):
+    g = lib.w4a8_gemm
+    assert g(A, B, C, D, E, 8, 64, 256, 128, A, 0, NUL) == ERR_UNSUPPORTED  # group
+    assert g(A, B, C, D, E, 8, 60, 256, 64, A, 0, NUL) == ERR_SHAPE        # n % 16
+    assert g(A, B, C, D, E, 8, 64, 200, 64, A, 0, NUL) == ERR_SHAPE        # k % 64
+    assert g(A, B, C, D, E, -1, 64, 256, 64, A, 0, NUL) == ERR_SHAPE
+    assert g(A, B, C, D, E, 8, 64, 150976 + 64, 64, A, 0, NUL) == ERR_UNSUPPORTED  # K_MAX
+    assert g(A, B, C, D, E, 8, 64, 256, 64, A, 7, NUL) == ERR_UNSUPPORTED  # out dtype
+    assert g(NUL, B, C, D, E, 8, 64, 256, 64, A, 0, NUL) == ERR_NULL
+    assert g(A, NUL, C, D, E, 8, 64, 256, 64, A, 0, NUL) == ERR_NULL
+    assert g(A, B, C, D, NUL, 8, 64, 256, 64, A, 0, NUL) == ERR_NULL
+    assert g(A, B, C, D, E, 8, 64, 256, 64, NUL, 0, NUL) == ERR_NULL
+    assert g(A, B, MIS, D, E, 8, 64, 256, 64, A, 0, NUL) == ERR_MISALIGNED
+    assert g(NUL, NUL, NUL, NUL, NUL, 0, 64, 256, 64, NUL, 1, NUL) == OK   # m == 0
+
+
+def test_bf16act_workspace_and_validation(lib):
+    ws = lib.w4a8_gemm_bf16act_workspace_bytes
+    assert ws(8, 4096) == 8 * 4096 + 256
+    assert ws(3, 64) == 256 + 256
+    assert ws(0, 64) == 0
+    f = lib.w4a8_gemm_bf16act
+    need = ws(8, 4096)
+    assert f(A, B, C, D, 8, 64, 4096, 64, E, 1, A, need - 1, NUL) == ERR_SHAPE
+    assert f(A, B, C, D, 8, 64, 4096, 64, E, 1, NUL, need, NUL) == ERR_NULL
+    assert f(A, B, C, D, 8, 64, 4096, 64, E, 1, MIS, need, NUL) == ERR_MISALIGNED
+    assert f(A, B, C, D, 8, 64, 0, 64, E, 1, A, need, NUL) == ERR_SHAPE    # k == 0
+    assert f(A, B, C, D, 8, 64, 4096, 32, E, 1, A, need, NUL) == ERR_UNSUPPORTED

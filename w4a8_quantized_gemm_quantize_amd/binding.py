@@ -1,0 +1,200 @@
+"""Thin Python binding of libw4a8.so (C ABI in include/w4a8.h).
+
+Argument marshalling only: torch tensors (device memory) become raw pointers,
+the current torch stream becomes the hipStream_t, and a non-OK status raises.
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback.  Importing this module loads the library and raises ImportError if
+it has not been built (``python -m w4a8_quantized_gemm_quantize_amd.build_lib``
+or ``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4a8.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libw4a8.so is not built ({LIB_PATH}); run build_lib.py first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP = range(6)
+F32, BF16, I32 = 0, 1, 2
+GROUP = 64
+N_TILE = 16
+K_MAX = 150976
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SIGS = {
+    "w4a8_abi_version": ([], ctypes.c_int32),
+    "w4a8_pack_layout_version": ([], ctypes.c_int32),
+    "w4a8_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "quantize_act_blockwise": ([_P, _I64, _I64, _I32, _P, _P, _P], ctypes.c_int),
+    "dequantize_act_blockwise": ([_P, _P, _I64, _I64, _I32, _P, ctypes.c_int, _P], ctypes.c_int),
+    "pack_w4_grouped": ([_P, _I64, _I64, _I32, _P, _P, _P, _P], ctypes.c_int),
+    "unpack_w4_grouped": ([_P, _P, _I64, _I64, _I32, _P, _P, _P], ctypes.c_int),
+    "w4a8_gemm": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, ctypes.c_int, _P],
+                  ctypes.c_int),
+    "w4a8_gemm_bf16act_workspace_bytes": ([_I64, _I64], ctypes.c_size_t),
+    "w4a8_gemm_bf16act": ([_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, ctypes.c_int, _P,
+                           ctypes.c_size_t, _P], ctypes.c_int),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+EXPORTED = tuple(_SIGS)
+
+
+class W4A8Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+def abi_version() -> int:
+    return int(_lib.w4a8_abi_version())
+
+
+def pack_layout_version() -> int:
+    return int(_lib.w4a8_pack_layout_version())
+
+
+def status_string(status: int) -> str:
+    return _lib.w4a8_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn, status):
+    if status != OK:
+        raise W4A8Error(fn, status)
+
+
+def _dev(t, dtype, name):
+    if not (t.is_cuda and t.dtype == dtype and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor")
+
+
+# ------------------------------------------------------------ activations --
+
+def quantize_act_blockwise(x: torch.Tensor, block: int, q=None, scales=None, stream=None):
+    """x bf16 [rows, cols] -> (q int8 [rows, cols], scales f32 [rows, cols // block])."""
+    _dev(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // block if block > 0 else 0), dtype=torch.float32,
+                             device=x.device)
+    _check("quantize_act_blockwise",
+           _lib.quantize_act_blockwise(_ptr(x), rows, cols, block, _ptr(q), _ptr(scales),
+                                       _stream(stream)))
+    return q, scales
+
+
+def dequantize_act_blockwise(q: torch.Tensor, scales: torch.Tensor, block: int,
+                             out_dtype=torch.float32, out=None, stream=None):
+    """-> x_hat [rows, cols] as float32 or bfloat16."""
+    _dev(q, torch.int8, "q")
+    _dev(scales, torch.float32, "scales")
+    rows, cols = q.shape
+    code = {torch.float32: F32, torch.bfloat16: BF16}[out_dtype]
+    if out is None:
+        out = torch.empty((rows, cols), dtype=out_dtype, device=q.device)
+    _check("dequantize_act_blockwise",
+           _lib.dequantize_act_blockwise(_ptr(q), _ptr(scales), rows, cols, block, _ptr(out),
+                                         code, _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------- weights --
+
+def pack_w4_grouped(w: torch.Tensor, group: int = GROUP, stream=None):
+    """w bf16 [n, k] -> (w_packed uint8 [n*k/2], grp_scale uint8 [n*k/group], ch_scale f32 [n])."""
+    _dev(w, torch.bfloat16, "w")
+    n, k = w.shape
+    dev = w.device
+    w_packed = torch.empty((n * k // 2,), dtype=torch.uint8, device=dev)
+    grp_scale = torch.empty((n * (k // group) if group > 0 else 0,), dtype=torch.uint8,
+                            device=dev)
+    ch_scale = torch.empty((n,), dtype=torch.float32, device=dev)
+    _check("pack_w4_grouped",
+           _lib.pack_w4_grouped(_ptr(w), n, k, group, _ptr(w_packed), _ptr(grp_scale),
+                                _ptr(ch_scale), _stream(stream)))
+    return w_packed, grp_scale, ch_scale
+
+
+def unpack_w4_grouped(w_packed, grp_scale, n: int, k: int, group: int = GROUP, stream=None):
+    """Test hook: packed layout -> (q int8 [n, k], s_g uint8 [n, k/group]) canonical."""
+    dev = w_packed.device
+    q = torch.empty((n, k), dtype=torch.int8, device=dev)
+    s_g = torch.empty((n, k // group), dtype=torch.uint8, device=dev)
+    _check("unpack_w4_grouped",
+           _lib.unpack_w4_grouped(_ptr(w_packed), _ptr(grp_scale), n, k, group, _ptr(q),
+                                  _ptr(s_g), _stream(stream)))
+    return q, s_g
+
+
+# ------------------------------------------------------------------- GEMM --
+
+_OUT = {torch.float32: F32, torch.bfloat16: BF16, torch.int32: I32}
+
+
+def w4a8_gemm(a_q, a_scale, w_packed, grp_scale, ch_scale, n: int, out_dtype=torch.bfloat16,
+              group: int = GROUP, out=None, stream=None):
+    """a_q int8 [m, k], a_scale f32 [m] -> out [m, n] (float32, bfloat16 or raw int32 acc)."""
+    _dev(a_q, torch.int8, "a_q")
+    m, k = a_q.shape
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a_q.device)
+    _check("w4a8_gemm",
+           _lib.w4a8_gemm(_ptr(a_q), _ptr(a_scale), _ptr(w_packed), _ptr(grp_scale),
+                          _ptr(ch_scale), m, n, k, group, _ptr(out), _OUT[out.dtype],
+                          _stream(stream)))
+    return out
+
+
+def workspace_bytes(m: int, k: int) -> int:
+    return int(_lib.w4a8_gemm_bf16act_workspace_bytes(m, k))
+
+
+def w4a8_gemm_bf16act(a, w_packed, grp_scale, ch_scale, n: int, out_dtype=torch.bfloat16,
+                      group: int = GROUP, out=None, workspace=None, stream=None):
+    """a bf16 [m, k] -> out [m, n]; per-token quantization into `workspace` then the GEMM."""
+    _dev(a, torch.bfloat16, "a")
+    m, k = a.shape
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    need = workspace_bytes(m, k)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=a.device)
+    _check("w4a8_gemm_bf16act",
+           _lib.w4a8_gemm_bf16act(_ptr(a), _ptr(w_packed), _ptr(grp_scale), _ptr(ch_scale), m,
+                                  n, k, group, _ptr(out), _OUT[out.dtype], _ptr(workspace),
+                                  workspace.numel(), _stream(stream)))
+    return out
+
+
+def workspace_views(workspace, m: int, k: int):
+    """(a_q [m, k] int8, a_scale [m] f32) views of a w4a8_gemm_bf16act workspace."""
+    off = (m * k + 255) // 256 * 256
+    a_q = workspace[: m * k].view(torch.int8).view(m, k)
+    a_s = workspace[off: off + 4 * m].view(torch.float32)
+    return a_q, a_s

@@ -1,0 +1,176 @@
+// abi.hip -- the extern "C" entry points of libw4a8.so (declared in w4a8.h):
+// argument validation, variant choice and launch on the caller's stream.
+// Nothing here allocates device memory or keeps state between calls.
+#include <stdlib.h>
+#include <string.h>
+
+#include "w4a8.h"
+#include "launch.hpp"
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool debug_sync_enabled() {
+    const char *v = getenv("W4A8_DEBUG");
+    return v && v[0] == '1';
+}
+
+// Map a launch result to a status; with W4A8_DEBUG=1 also wait for the stream.
+w4a8_status finish(hipError_t launched, hipStream_t stream) {
+    if (launched != hipSuccess) return W4A8_ERR_HIP;
+    if (debug_sync_enabled()) {
+        if (hipStreamSynchronize(stream) != hipSuccess) return W4A8_ERR_HIP;
+        if (hipGetLastError() != hipSuccess) return W4A8_ERR_HIP;
+    }
+    return W4A8_OK;
+}
+
+w4a8_status check_act_shape(int64_t rows, int64_t cols, int32_t block) {
+    if (rows < 0 || cols < 0 || block <= 0 || (block % 8) != 0 || (cols % block) != 0)
+        return W4A8_ERR_SHAPE;
+    return W4A8_OK;
+}
+
+w4a8_status check_weight_shape(int64_t n, int64_t k, int32_t group) {
+    if (n < 0 || k < 0) return W4A8_ERR_SHAPE;
+    if (group != W4A8_GROUP) return W4A8_ERR_UNSUPPORTED;
+    if ((n % W4A8_N_TILE) != 0 || (k % W4A8_GROUP) != 0) return W4A8_ERR_SHAPE;
+    return W4A8_OK;
+}
+
+// Shared checks of the GEMM entry points.  `a` is the activation pointer (int8
+// codes or bf16); `a_scale` is only required when need_a_scale is set.
+w4a8_status check_gemm_args(const void *a, const float *a_scale, bool need_a_scale,
+                            const uint8_t *w_packed, const uint8_t *grp_scale,
+                            const float *ch_scale, int64_t m, int64_t n, int64_t k,
+                            int32_t group, const void *out, w4a8_dtype out_dtype) {
+    if (m < 0) return W4A8_ERR_SHAPE;
+    w4a8_status st = check_weight_shape(n, k, group);
+    if (st != W4A8_OK) return st;
+    if (k > W4A8_K_MAX) return W4A8_ERR_UNSUPPORTED;
+    if (out_dtype != W4A8_F32 && out_dtype != W4A8_BF16 && out_dtype != W4A8_I32)
+        return W4A8_ERR_UNSUPPORTED;
+    if (m == 0 || n == 0) return W4A8_OK;
+    const bool has_k = k > 0;
+    if ((has_k && (!a || !w_packed || !grp_scale)) || !ch_scale || !out ||
+        (need_a_scale && !a_scale))
+        return W4A8_ERR_NULL;
+    if ((has_k && (!aligned16(a) || !aligned16(w_packed) || !aligned16(grp_scale))) ||
+        !aligned16(ch_scale) || !aligned16(out) || (need_a_scale && !aligned16(a_scale)))
+        return W4A8_ERR_MISALIGNED;
+    return W4A8_OK;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t w4a8_abi_version(void) { return W4A8_ABI_VERSION; }
+
+int32_t w4a8_pack_layout_version(void) { return W4A8_PACK_LAYOUT_V1; }
+
+const char *w4a8_status_string(w4a8_status status) {
+    switch (status) {
+        case W4A8_OK: return "ok";
+        case W4A8_ERR_NULL: return "null pointer";
+        case W4A8_ERR_SHAPE: return "invalid shape";
+        case W4A8_ERR_UNSUPPORTED: return "unsupported argument";
+        case W4A8_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+        case W4A8_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+w4a8_status quantize_act_blockwise(const uint16_t *x, int64_t rows, int64_t cols, int32_t block,
+                                   int8_t *q, float *scales, hipStream_t stream) {
+    w4a8_status st = check_act_shape(rows, cols, block);
+    if (st != W4A8_OK) return st;
+    if (rows == 0 || cols == 0) return W4A8_OK;
+    if (!x || !q || !scales) return W4A8_ERR_NULL;
+    if (!aligned16(x) || !aligned16(q) || !aligned16(scales)) return W4A8_ERR_MISALIGNED;
+    return finish(w4a8::launch_quantize_act(x, rows, cols, block, q, scales, stream), stream);
+}
+
+w4a8_status dequantize_act_blockwise(const int8_t *q, const float *scales, int64_t rows,
+                                     int64_t cols, int32_t block, void *out,
+                                     w4a8_dtype out_dtype, hipStream_t stream) {
+    w4a8_status st = check_act_shape(rows, cols, block);
+    if (st != W4A8_OK) return st;
+    if (out_dtype != W4A8_F32 && out_dtype != W4A8_BF16) return W4A8_ERR_UNSUPPORTED;
+    if (rows == 0 || cols == 0) return W4A8_OK;
+    if (!q || !scales || !out) return W4A8_ERR_NULL;
+    if (!aligned16(q) || !aligned16(scales) || !aligned16(out)) return W4A8_ERR_MISALIGNED;
+    return finish(w4a8::launch_dequantize_act(q, scales, rows, cols, block, out,
+                                              out_dtype == W4A8_BF16, stream),
+                  stream);
+}
+
+w4a8_status pack_w4_grouped(const uint16_t *w, int64_t n, int64_t k, int32_t group,
+                            uint8_t *w_packed, uint8_t *grp_scale, float *ch_scale,
+                            hipStream_t stream) {
+    w4a8_status st = check_weight_shape(n, k, group);
+    if (st != W4A8_OK) return st;
+    if (n == 0) return W4A8_OK;
+    if (!ch_scale || (k > 0 && (!w || !w_packed || !grp_scale))) return W4A8_ERR_NULL;
+    if (!aligned16(ch_scale) ||
+        (k > 0 && (!aligned16(w) || !aligned16(w_packed) || !aligned16(grp_scale))))
+        return W4A8_ERR_MISALIGNED;
+    return finish(w4a8::launch_pack_w4(w, n, k, w_packed, grp_scale, ch_scale, stream), stream);
+}
+
+w4a8_status unpack_w4_grouped(const uint8_t *w_packed, const uint8_t *grp_scale, int64_t n,
+                              int64_t k, int32_t group, int8_t *q, uint8_t *s_g,
+                              hipStream_t stream) {
+    w4a8_status st = check_weight_shape(n, k, group);
+    if (st != W4A8_OK) return st;
+    if (n == 0 || k == 0) return W4A8_OK;
+    if (!w_packed || !grp_scale || !q || !s_g) return W4A8_ERR_NULL;
+    if (!aligned16(w_packed) || !aligned16(grp_scale) || !aligned16(q) || !aligned16(s_g))
+        return W4A8_ERR_MISALIGNED;
+    return finish(w4a8::launch_unpack_w4(w_packed, grp_scale, n, k, q, s_g, stream), stream);
+}
+
+w4a8_status w4a8_gemm(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
+                      const uint8_t *grp_scale, const float *ch_scale, int64_t m, int64_t n,
+                      int64_t k, int32_t group, void *out, w4a8_dtype out_dtype,
+                      hipStream_t stream) {
+    w4a8_status st = check_gemm_args(a_q, a_scale, true, w_packed, grp_scale, ch_scale, m, n,
+                                     k, group, out, out_dtype);
+    if (st != W4A8_OK) return st;
+    if (m == 0 || n == 0) return W4A8_OK;
+    return finish(w4a8::launch_w4a8_gemm(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k,
+                                         out, (int)out_dtype, stream),
+                  stream);
+}
+
+size_t w4a8_gemm_bf16act_workspace_bytes(int64_t m, int64_t k) {
+    if (m <= 0 || k <= 0) return 0;
+    return round_up((size_t)m * (size_t)k, 256) + round_up((size_t)m * sizeof(float), 256);
+}
+
+w4a8_status w4a8_gemm_bf16act(const uint16_t *a, const uint8_t *w_packed,
+                              const uint8_t *grp_scale, const float *ch_scale, int64_t m,
+                              int64_t n, int64_t k, int32_t group, void *out,
+                              w4a8_dtype out_dtype, void *workspace, size_t ws_bytes,
+                              hipStream_t stream) {
+    if (k <= 0 || m < 0) return W4A8_ERR_SHAPE;
+    w4a8_status st = check_gemm_args(a, nullptr, false, w_packed, grp_scale, ch_scale, m, n,
+                                     k, group, out, out_dtype);
+    if (st != W4A8_OK) return st;
+    if (m == 0 || n == 0) return W4A8_OK;
+    if (!workspace) return W4A8_ERR_NULL;
+    if (!aligned16(workspace)) return W4A8_ERR_MISALIGNED;
+    if (ws_bytes < w4a8_gemm_bf16act_workspace_bytes(m, k)) return W4A8_ERR_SHAPE;
+    int8_t *a_q = (int8_t *)workspace;
+    float *a_s = (float *)((uint8_t *)workspace + round_up((size_t)m * (size_t)k, 256));
+    hipError_t e = w4a8::launch_quantize_act(a, m, k, (int32_t)k, a_q, a_s, stream);
+    if (e != hipSuccess) return W4A8_ERR_HIP;
+    return finish(w4a8::launch_w4a8_gemm(a_q, a_s, w_packed, grp_scale, ch_scale, m, n, k, out,
+                                         (int)out_dtype, stream),
+                  stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// device_common.hpp -- helpers shared by the gfx950 kernels of libw4a8.so.
+//
+// Packed weight layout V1 (written by pack_w4_grouped, read by the GEMMs):
+//   Output channels are grouped in tiles of 16 (t = n / 16, c = n % 16) and K
+//   in chunks of 128 (j = k / 128; the last chunk is 64 wide when k % 128 == 64).
+//   Inside a chunk, the 64 lanes of a wavefront each own one record:
+//     lane = c + 16 * kq,   kq = (k % 64) / 16
+//   A full chunk stores 16 bytes per lane (record at lane * 16): bytes 0..7 hold
+//   the 16 weights of K-step h = 0 (k % 128 < 64), bytes 8..15 those of h = 1.
+//   A half chunk stores 8 bytes per lane (record at lane * 8), step 0 only.
+//   The 8 bytes of one step are two 32-bit words P0, P1; with e = k % 16:
+//     e = 0..3   -> low  nibble of byte e     of P0
+//     e = 4..7   -> high nibble of byte e - 4 of P0
+//     e = 8..11  -> low  nibble of byte e - 8 of P1
+//     e = 12..15 -> high nibble of byte e - 12 of P1
+//   so (P & 0x0F0F0F0F) and ((P >> 4) & 0x0F0F0F0F) are four consecutive k in
+//   byte order: exactly the 16-byte per-lane operand of v_mfma_i32_16x16x64_i8
+//   for 16 output channels and 64 k.  A tile occupies 16 * k / 2 bytes and
+//   chunk j starts at byte j * 1024 of its tile.
+//   Nibbles hold u = q + 8 (q in [-7, 7]).
+// Group scales in kernel order: byte [t][g][c] at t * 16 * G + g * 16 + c
+// (G = k / 64), i.e. the 16 channels of a tile are contiguous per group.
+//
+// Rebuilding the int8 operand of one step for one lane (LiquidGEMM verdict
+// page, pith_extraction.key_machinery, symmetric instance): per byte
+//   v = u * s + (128 - 8 s)  stays in [16, 240] (no carry between bytes)
+//   v XOR 0x80 read as int8 = (u - 8) * s = q * s in [-112, 112].
+// The multiply-add runs on 16-bit halves (v_pk_mad_u16), two bytes per half.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a8 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+
+constexpr int kGroup = 64;
+constexpr int kNTile = 16;
+constexpr int kChunkK = 128;
+constexpr int kChunkBytes = 1024;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// binary32 -> bf16 bits, round to nearest even; NaN kept as a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// round-half-even of v, saturated to [-lim, lim]; NaN gives 0.
+__device__ __forceinline__ int sat_rne_code(float v, float lim) {
+    float r = __builtin_rintf(v);
+    r = __builtin_fminf(__builtin_fmaxf(r, -lim), lim);
+    r = (v == v) ? r : 0.0f;
+    return (int)r;
+}
+
+// Rebuild 4 int8 weights q*s from a word of 4 nibbles (one per byte, low bits).
+// mul = s | s << 16, add = (128 - 8 s) * 0x01010101.
+__device__ __forceinline__ int dequant4(uint32_t nib, uint32_t mul, uint32_t add) {
+    v2u16 x = __builtin_bit_cast(v2u16, nib);
+    v2u16 m = __builtin_bit_cast(v2u16, mul);
+    v2u16 a = __builtin_bit_cast(v2u16, add);
+    v2u16 r = x * m + a;
+    return (int)(__builtin_bit_cast(uint32_t, r) ^ 0x80808080u);
+}
+
+__device__ __forceinline__ void scale_consts(uint32_t s, uint32_t &mul, uint32_t &add) {
+    mul = s | (s << 16);
+    uint32_t off = 128u - 8u * s;
+    off |= off << 8;
+    add = off | (off << 16);
+}
+
+// 16 packed weights of one K-step (two words) -> the 16-byte MFMA operand.
+__device__ __forceinline__ v4i unpack_step(uint32_t p0, uint32_t p1, uint32_t mul,
+                                           uint32_t add) {
+    v4i r;
+    r.x = dequant4(p0 & 0x0F0F0F0Fu, mul, add);
+    r.y = dequant4((p0 >> 4) & 0x0F0F0F0Fu, mul, add);
+    r.z = dequant4(p1 & 0x0F0F0F0Fu, mul, add);
+    r.w = dequant4((p1 >> 4) & 0x0F0F0F0Fu, mul, add);
+    return r;
+}
+
+__device__ __forceinline__ v4i mfma16x16x64(v4i a, v4i b, v4i c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// Byte offset of chunk j of n-tile t in the packed weights.
+__device__ __forceinline__ int64_t packed_chunk_offset(int64_t t, int64_t j, int64_t k) {
+    return t * (int64_t)kNTile * k / 2 + j * kChunkBytes;
+}
+
+}  // namespace w4a8

@@ -1,0 +1,23 @@
+// launch.hpp -- internal launchers behind the C ABI (arguments already validated).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a8 {
+
+hipError_t launch_quantize_act(const uint16_t *x, int64_t rows, int64_t cols, int32_t block,
+                               int8_t *q, float *scales, hipStream_t stream);
+hipError_t launch_dequantize_act(const int8_t *q, const float *scales, int64_t rows,
+                                 int64_t cols, int32_t block, void *out, bool bf16,
+                                 hipStream_t stream);
+hipError_t launch_pack_w4(const uint16_t *w, int64_t n, int64_t k, uint8_t *w_packed,
+                          uint8_t *grp_scale, float *ch_scale, hipStream_t stream);
+hipError_t launch_unpack_w4(const uint8_t *w_packed, const uint8_t *grp_scale, int64_t n,
+                            int64_t k, int8_t *q, uint8_t *s_g, hipStream_t stream);
+// out_dtype: 0 = binary32, 1 = bf16, 2 = int32 accumulator
+hipError_t launch_w4a8_gemm(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
+                            const uint8_t *grp_scale, const float *ch_scale, int64_t m,
+                            int64_t n, int64_t k, void *out, int out_dtype, hipStream_t stream);
+
+}  // namespace w4a8

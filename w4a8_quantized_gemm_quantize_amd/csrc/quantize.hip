@@ -1,0 +1,230 @@
+// quantize.hip -- block-wise absmax int8 quantization of bf16 activations and
+// its dequantization, for gfx950.
+//
+// Method: "EQuARX" verdict page (pith.science arXiv 2506.17615),
+// pith_extraction.key_machinery -- one binary32 scale per block from the
+// block's absolute maximum (phase 1), then the data scaled and rounded to int8
+// (phase 2); dequantization multiplies back to binary32.  Both phases run in
+// one pass: each element is read from HBM once, kept in registers while the
+// block maximum is reduced across lanes, then scaled and stored.
+//
+// Per block: s = amax / 127, inv = 127 / amax (0 when amax == 0),
+// q = clamp(rne(x * inv), -127, 127), NaN products give 0.  Both divisions are
+// correctly rounded binary32 divisions (HIP's default) and nothing is
+// contracted (-ffp-contract=off), so codes and scales are exact functions of
+// the bf16 input.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace w4a8 {
+namespace {
+
+// 8 bf16 (one 16-byte load) -> 8 floats.
+__device__ __forceinline__ void load8(const u32x4 &v, float f[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
+__device__ __forceinline__ float absmax8(const float f[8]) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(f[i]));
+    return m;
+}
+
+// 8 floats * inv -> 8 int8 codes packed little-endian in two words.
+__device__ __forceinline__ u32x2 codes8(const float f[8], float inv) {
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int c = sat_rne_code(f[i] * inv, 127.0f);
+        w[i >> 2] |= ((uint32_t)c & 0xffu) << (8 * (i & 3));
+    }
+    return u32x2{w[0], w[1]};
+}
+
+__device__ __forceinline__ void scale_pair(float amax, float &s, float &inv) {
+    s = amax / 127.0f;
+    inv = (amax > 0.0f) ? (127.0f / amax) : 0.0f;
+}
+
+// Blocks of 8 * LPB elements (LPB = 1..64 lanes, a power of two).  The tensor
+// is a flat sequence of blocks (cols % block == 0), so thread i owns the
+// 16-byte vector i and the LPB lanes of one block are adjacent in a wavefront.
+template <int LPB>
+__global__ __launch_bounds__(256) void quant_pow2_kernel(const u32x4 *__restrict__ x,
+                                                         int64_t nvec, u32x2 *__restrict__ q,
+                                                         float *__restrict__ scales) {
+    constexpr int U = 4;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += U * stride) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int64_t idx = i + u * stride;
+            if (idx < nvec) v[u] = __builtin_nontemporal_load(&x[idx]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int64_t idx = i + u * stride;
+            // nvec is a multiple of LPB, so a block's lanes agree on this branch.
+            if (idx < nvec) {
+                float f[8];
+                load8(v[u], f);
+                float amax = absmax8(f);
+#pragma unroll
+                for (int off = 1; off < LPB; off <<= 1)
+                    amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
+                float s, inv;
+                scale_pair(amax, s, inv);
+                q[idx] = codes8(f, inv);
+                if ((idx & (LPB - 1)) == 0) scales[idx / LPB] = s;
+            }
+        }
+    }
+}
+
+// Any block that is a multiple of 8: one 256-thread workgroup per block.  Up
+// to 256 * MAXV vectors stay in registers between the two phases; a longer
+// block is read a second time (from cache) for phase 2.
+template <int MAXV>
+__global__ __launch_bounds__(256) void quant_wide_kernel(const u32x4 *__restrict__ x,
+                                                         int64_t nblocks, int64_t block_vecs,
+                                                         u32x2 *__restrict__ q,
+                                                         float *__restrict__ scales) {
+    __shared__ float red[4];
+    const int tid = threadIdx.x;
+    for (int64_t b = blockIdx.x; b < nblocks; b += gridDim.x) {
+        const int64_t base = b * block_vecs;
+        u32x4 v[MAXV];
+        float amax = 0.0f;
+#pragma unroll
+        for (int u = 0; u < MAXV; ++u) {
+            int64_t idx = tid + (int64_t)u * 256;
+            if (idx < block_vecs) {
+                v[u] = x[base + idx];
+                float f[8];
+                load8(v[u], f);
+                amax = __builtin_fmaxf(amax, absmax8(f));
+            }
+        }
+        for (int64_t idx = tid + (int64_t)MAXV * 256; idx < block_vecs; idx += 256) {
+            float f[8];
+            load8(x[base + idx], f);
+            amax = __builtin_fmaxf(amax, absmax8(f));
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
+        if ((tid & 63) == 0) red[tid >> 6] = amax;
+        __syncthreads();
+        amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+        __syncthreads();
+        float s, inv;
+        scale_pair(amax, s, inv);
+#pragma unroll
+        for (int u = 0; u < MAXV; ++u) {
+            int64_t idx = tid + (int64_t)u * 256;
+            if (idx < block_vecs) {
+                float f[8];
+                load8(v[u], f);
+                q[base + idx] = codes8(f, inv);
+            }
+        }
+        for (int64_t idx = tid + (int64_t)MAXV * 256; idx < block_vecs; idx += 256) {
+            float f[8];
+            load8(x[base + idx], f);
+            q[base + idx] = codes8(f, inv);
+        }
+        if (tid == 0) scales[b] = s;
+    }
+}
+
+// out = q * s (binary32), optionally rounded to bf16.  Thread i owns 8 codes.
+template <bool BF16>
+__global__ __launch_bounds__(256) void dequant_kernel(const u32x2 *__restrict__ q,
+                                                      const float *__restrict__ scales,
+                                                      int64_t nvec, int64_t block_vecs,
+                                                      void *__restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
+        u32x2 c = __builtin_nontemporal_load(&q[i]);
+        float s = scales[i / block_vecs];
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            uint32_t w = e < 4 ? c.x : c.y;
+            int8_t b = (int8_t)((w >> (8 * (e & 3))) & 0xffu);
+            f[e] = (float)b * s;
+        }
+        if (BF16) {
+            u32x4 o;
+            o.x = f32_to_bf16_rne(f[0]) | (f32_to_bf16_rne(f[1]) << 16);
+            o.y = f32_to_bf16_rne(f[2]) | (f32_to_bf16_rne(f[3]) << 16);
+            o.z = f32_to_bf16_rne(f[4]) | (f32_to_bf16_rne(f[5]) << 16);
+            o.w = f32_to_bf16_rne(f[6]) | (f32_to_bf16_rne(f[7]) << 16);
+            __builtin_nontemporal_store(o, &((u32x4 *)out)[i]);
+        } else {
+            f32x4 *o = (f32x4 *)out;
+            __builtin_nontemporal_store(f32x4{f[0], f[1], f[2], f[3]}, &o[2 * i]);
+            __builtin_nontemporal_store(f32x4{f[4], f[5], f[6], f[7]}, &o[2 * i + 1]);
+        }
+    }
+}
+
+int grid_for(int64_t work_items, int per_thread) {
+    int64_t threads = (work_items + per_thread - 1) / per_thread;
+    int64_t blocks = (threads + 255) / 256;
+    const int64_t cap = 256 * 32;  // 32 workgroups per CU over 256 CUs
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    return (int)blocks;
+}
+
+}  // namespace
+
+hipError_t launch_quantize_act(const uint16_t *x, int64_t rows, int64_t cols, int32_t block,
+                               int8_t *q, float *scales, hipStream_t stream) {
+    const int64_t nvec = rows * cols / 8;
+    const u32x4 *xv = (const u32x4 *)x;
+    u32x2 *qv = (u32x2 *)q;
+    if (nvec == 0) return hipSuccess;
+    const int lpb = block / 8;
+    const int g = grid_for(nvec, 4);
+    switch (block) {
+        case 8: quant_pow2_kernel<1><<<g, 256, 0, stream>>>(xv, nvec, qv, scales); break;
+        case 16: quant_pow2_kernel<2><<<g, 256, 0, stream>>>(xv, nvec, qv, scales); break;
+        case 32: quant_pow2_kernel<4><<<g, 256, 0, stream>>>(xv, nvec, qv, scales); break;
+        case 64: quant_pow2_kernel<8><<<g, 256, 0, stream>>>(xv, nvec, qv, scales); break;
+        case 128: quant_pow2_kernel<16><<<g, 256, 0, stream>>>(xv, nvec, qv, scales); break;
+        case 256: quant_pow2_kernel<32><<<g, 256, 0, stream>>>(xv, nvec, qv, scales); break;
+        case 512: quant_pow2_kernel<64><<<g, 256, 0, stream>>>(xv, nvec, qv, scales); break;
+        default: {
+            const int64_t nblocks = rows * (cols / block);
+            int64_t grid = nblocks < 65536 ? nblocks : 65536;
+            quant_wide_kernel<16><<<(int)grid, 256, 0, stream>>>(xv, nblocks, (int64_t)lpb, qv,
+                                                                 scales);
+        }
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize_act(const int8_t *q, const float *scales, int64_t rows,
+                                 int64_t cols, int32_t block, void *out, bool bf16,
+                                 hipStream_t stream) {
+    const int64_t nvec = rows * cols / 8;
+    if (nvec == 0) return hipSuccess;
+    const int g = grid_for(nvec, 4);
+    if (bf16)
+        dequant_kernel<true><<<g, 256, 0, stream>>>((const u32x2 *)q, scales, nvec, block / 8,
+                                                    out);
+    else
+        dequant_kernel<false><<<g, 256, 0, stream>>>((const u32x2 *)q, scales, nvec, block / 8,
+                                                     out);
+    return hipGetLastError();
+}
+
+}  // namespace w4a8
