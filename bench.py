@@ -1,0 +1,280 @@
+"""Benchmark of the W4A8 hot path on one MI355X.
+
+Default workload (decode-shaped, HBM-bound): A bf16 [8, 4096] ~ N(0,1) with 0.1%
+outliers x20, W bf16 [4096, 4096] ~ N(0, 0.02^2) packed once to two-level int4
+(group 64).  One step = w4a8_gemm_bf16act: per-token int8 quantization of A plus
+the W4A8 GEMM with bf16 output (for m <= 16 one kernel does both).  Weight
+packing is offline (once per weight) and not part of a step.  The steps are
+captured into a HIP graph and the timed region replays it, so host-side launch
+cost does not stand in for device time.
+
+Inputs are resident in HBM before timing.  To keep the 256 MB MALL and the L2s
+from serving the weights, each step uses the next of R distinct copies of the
+packed weights and activations (R copies total > 512 MB).
+
+Printed: one JSON line with the step throughput (TOPS = 2*M*N*K / step time),
+the dominant kernel's roofline (algorithmic bytes per launch / average launch
+time from HIP events on the launch stream), the standalone quantizer workload
+(64M bf16 elements, block 32 and 128: GB/s), and the CPU oracle timed on the
+host cores on a bounded sample (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, vendor figure
+INT8_PEAK_TOPS = 5000.0       # MI355X dense int8 MFMA, vendor figure
+METRIC = "W4A8 GEMM TOPS + quantizer GB/s; % of int8-MFMA / HBM roofline, 1 MI355X"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="decode",
+                   choices=["decode", "prefill", "ffn_down_m1", "ffn_down_m64", "ffn_down_m2048",
+                            "tiny"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-quantizer", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def gemm_algorithmic_bytes(m, n, k, out_bytes, fused):
+    """Bytes the W4A8 GEMM must move: int4 weights, uint8 group scales, fp32 channel
+    scales and the output, each once; plus the activations: bf16 in and the int8
+    codes + fp32 row scales out when quantization is fused into the kernel, else
+    the int8 codes + row scales in."""
+    act = (2 * m * k + m * k + 4 * m) if fused else (m * k + 4 * m)
+    return n * k // 2 + n * (k // 64) + 4 * n + act + m * n * out_bytes
+
+
+def quantizer_algorithmic_bytes(elems, block):
+    """bf16 in (2 B), int8 out (1 B), one fp32 scale per block."""
+    return elems * 3 + 4 * (elems // block)
+
+
+def profile_traffic(kernel_key: str, workload: str):
+    """HBM traffic per launch measured by rocprofv3 counters, if a committed profile
+    for this kernel and workload exists and the GEMM sources are unchanged since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_key}_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    msha = re.search(r"sources_sha256:\s*([0-9a-f]{64})", text)
+    mbytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (msha and mbytes) or msha.group(1) != sources_sha256():
+        return None
+    return float(mbytes.group(1))
+
+
+def sources_sha256() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "w4a8_quantized_gemm_quantize_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def cpu_baseline(a_bits, w_bits, spec, seconds):
+    """The CPU oracle (plain C, OpenMP over output rows), timed on the host cores:
+    per-token quantization + GEMM on the same workload, repeated for ~`seconds`."""
+    import oracle
+    m, n, k = spec["m"], spec["n"], spec["k"]
+    q, sg, sch = oracle.quantize_w4_grouped(w_bits, 64)          # offline, untimed
+    rows = m
+    if m > 64:                                                     # bound the sample
+        rows = 64
+    a = np.ascontiguousarray(a_bits[:rows])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.w4a8_gemm_bf16act(a, q, sg, sch, 64, want_y=True)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    ops = 2.0 * rows * n * k * reps
+    return {"value": ops / el / 1e12, "unit": "TOPS", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} runs of per-token quantize + GEMM on rows [0,{rows}) of the "
+                      f"{m}x{n}x{k} workload ({el:.1f} s wall)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build "
+              "runs the hot path on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from w4a8_quantized_gemm_quantize_amd import binding as w4a8
+    from w4a8_quantized_gemm_quantize_amd import inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    a_bits, w_bits, spec = inputs.workload_inputs(args.workload, seed=0)
+    m, n, k = spec["m"], spec["n"], spec["k"]
+    out_dtype = torch.bfloat16 if spec["out"] == "bf16" else torch.float32
+    out_bytes = 2 if spec["out"] == "bf16" else 4
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    a0 = to_dev(a_bits)
+    wp0, gs0, cs0 = w4a8.pack_w4_grouped(to_dev(w_bits))
+    per_copy = wp0.numel() + gs0.numel() + 4 * cs0.numel() + 2 * m * k
+    copies = max(2, min(64, (512 << 20) // per_copy + 1))
+    wps = [wp0] + [wp0.clone() for _ in range(copies - 1)]
+    gss = [gs0] + [gs0.clone() for _ in range(copies - 1)]
+    css = [cs0] + [cs0.clone() for _ in range(copies - 1)]
+    acts = [a0] + [a0.clone() for _ in range(copies - 1)]
+    wss = [torch.empty(w4a8.workspace_bytes(m, k), dtype=torch.uint8, device=dev)
+           for _ in range(copies)]
+    out = torch.empty((m, n), dtype=out_dtype, device=dev)
+
+    def step(r, stream):
+        # one pass of the path: per-token quantization of A + W4A8 GEMM
+        w4a8.w4a8_gemm_bf16act(acts[r], wps[r], gss[r], css[r], n, out=out, workspace=wss[r],
+                               stream=stream)
+
+    def gemm_only(r, stream):
+        a_q, a_s = w4a8.workspace_views(wss[r], m, k)
+        w4a8.w4a8_gemm(a_q, a_s, wps[r], gss[r], css[r], n, out=out, stream=stream)
+
+    # Warm up eagerly on a side stream, then capture `copies` steps (one per
+    # weight copy) into one HIP graph; the timed region replays it.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(max(args.warmup, copies)):
+            step(i % copies, side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            s = torch.cuda.current_stream()
+            for r in range(copies):
+                fn(r, s)
+        return g
+
+    g_step = capture(step)
+    reps = max(1, (args.steps + copies - 1) // copies)
+    steps = reps * copies
+    stream = torch.cuda.current_stream()
+    g_step.replay()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for _ in range(reps):
+        g_step.replay()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / steps
+
+    # Dominant kernel: with m <= 16 the step is one fused kernel (quantization in
+    # the GEMM's prologue), so its average duration is the step time; otherwise
+    # the GEMM launches alone are replayed from their own graph and timed.
+    fused = m <= 16
+    if fused:
+        gemm_ms = ms_per_step
+    else:
+        g_gemm = capture(gemm_only)
+        g_gemm.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g_gemm.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gemm_ms = e0.elapsed_time(e1) / steps
+
+    ops = 2.0 * m * n * k
+    tops = ops / (ms_per_step * 1e-3) / 1e12
+    gemm_bytes = gemm_algorithmic_bytes(m, n, k, out_bytes, fused)
+    hbm_bound = m <= 64
+    if hbm_bound:
+        achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS}
+    else:
+        achieved = ops / (gemm_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                "frac": achieved / INT8_PEAK_TOPS}
+    kernel_key = ("gemm_skinny_fused" if fused else "gemm_skinny") if hbm_bound else "gemm_tiled"
+    roof["kernel"] = kernel_key
+    roof["kernel_ms"] = gemm_ms
+    roof["algorithmic_bytes_per_launch"] = gemm_bytes
+    roof["traffic"] = profile_traffic(kernel_key, args.workload)
+
+    line = {
+        "metric": METRIC, "value": tops, "unit": "TOPS", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": f"{args.workload} W4A8 GEMM M={m} K={k} N={n}, per-token int8 "
+                               f"activations, int4 weights group 64, {spec['out']} out",
+                   "m": m, "n": n, "k": k, "group": 64, "weight_copies_rotated": copies,
+                   "hip_graph_steps": copies, "parallelism": "single GPU"},
+        "roofline": roof,
+    }
+
+    if not args.no_quantizer:
+        line["quantizer"] = quantizer_leg(torch, w4a8, inputs, dev, stream)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(a_bits, w_bits, spec, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def quantizer_leg(torch, w4a8, inputs, dev, stream, reps=20):
+    """Standalone quantizer workload: 64M bf16 ~ N(0,1) as [65536, 1024], blocks 32
+    and 128.  Two input/output sets alternate (2 x 200 MB) so reads come from HBM."""
+    spec = inputs.QUANTIZER
+    rows, cols = spec["rows"], spec["cols"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    xs = [torch.randn((rows, cols), generator=g, device=dev, dtype=torch.float32)
+          .to(torch.bfloat16) for _ in range(2)]
+    res = {"workload": f"{rows}x{cols} bf16 ~ N(0,1) (64M elements)"}
+    for block in spec["blocks"]:
+        qs = [torch.empty((rows, cols), dtype=torch.int8, device=dev) for _ in range(2)]
+        ss = [torch.empty((rows, cols // block), dtype=torch.float32, device=dev)
+              for _ in range(2)]
+        for i in range(4):
+            w4a8.quantize_act_blockwise(xs[i % 2], block, q=qs[i % 2], scales=ss[i % 2],
+                                        stream=stream)
+        times = []
+        for i in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            w4a8.quantize_act_blockwise(xs[i % 2], block, q=qs[i % 2], scales=ss[i % 2],
+                                        stream=stream)
+            e1.record(stream)
+            times.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in times]))
+        gbps = quantizer_algorithmic_bytes(rows * cols, block) / (ms * 1e-3) / 1e9
+        res[f"block{block}"] = {"kernel_ms": ms, "achieved": gbps, "unit": "GB/s",
+                                "frac": gbps / HBM_PEAK_GBPS}
+    return res
+
+
+if __name__ == "__main__":
+    main()

@@ -198,7 +198,15 @@ def test_gemm_extreme_codes_do_not_overflow(w4a8):
     assert (acc8.cpu().numpy().astype(np.int64) == 127 * 112 * k).all()
 
 
-@pytest.mark.parametrize("m,n,k", [(8, 4096, 4096), (3, 64, 192), (100, 96, 512)])
+@pytest.mark.parametrize("m,n,k", [
+    (8, 4096, 4096),     # decode shape: quantization fused into the GEMM kernel
+    (3, 64, 192),        # odd row count, trailing half chunk
+    (13, 48, 1024),
+    (1, 32, 49088),      # largest one-row K kept in LDS
+    (2, 32, 24512),
+    (16, 128, 4096),     # too large for the fused prologue: two kernels
+    (100, 96, 512),      # tiled GEMM path
+])
 def test_fused_bf16act_equals_two_calls(w4a8, m, n, k):
     announce("fused", m, n, k)
     _, dev_w, ref_w = _pack(w4a8, n, k, seed=7)
@@ -299,3 +307,39 @@ def test_workload_sampled(w4a8, name):
 @pytest.mark.parametrize("name", ["prefill", "ffn_down_m2048"])
 def test_large_workload_sampled(w4a8, name):
     _sampled_check(w4a8, name, n_rows=24, n_cols=48)
+
+
+# ------------------------------------------------------------ HIP graphs ----
+
+@pytest.mark.parametrize("m,n,k", [(8, 4096, 4096), (200, 256, 512)])
+def test_graph_replay_matches_eager(w4a8, m, n, k):
+    """Library calls captured into a HIP graph (as the benchmark does) replay to the
+    eager result every time, with eager work and synchronizations in between."""
+    announce("graph replay", m, n, k)
+    _, dev_w, _ = _pack(w4a8, n, k, seed=21)
+    a = to_dev_bf16(inputs.activations(m, k, seed=21, outlier_frac=0.001))
+    ws = torch.empty(w4a8.workspace_bytes(m, k), dtype=torch.uint8, device="cuda")
+    out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    acc = torch.empty((m, n), dtype=torch.int32, device="cuda")
+    eager = w4a8.w4a8_gemm_bf16act(a, *dev_w, n, out_dtype=torch.bfloat16).clone()
+    eager_acc = w4a8.w4a8_gemm_bf16act(a, *dev_w, n, out_dtype=torch.int32).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        w4a8.w4a8_gemm_bf16act(a, *dev_w, n, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w4a8.w4a8_gemm_bf16act(a, *dev_w, n, out=out, workspace=ws)
+        ws_q, ws_s = w4a8.workspace_views(ws, m, k)
+        w4a8.w4a8_gemm(ws_q, ws_s, *dev_w, n, out=acc)
+    for rep in range(4):
+        out.zero_()
+        acc.fill_(-1)
+        ws.fill_(0x55)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), rep
+        assert torch.equal(acc, eager_acc), rep

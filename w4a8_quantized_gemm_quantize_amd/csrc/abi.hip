@@ -166,10 +166,8 @@ w4a8_status w4a8_gemm_bf16act(const uint16_t *a, const uint8_t *w_packed,
     if (ws_bytes < w4a8_gemm_bf16act_workspace_bytes(m, k)) return W4A8_ERR_SHAPE;
     int8_t *a_q = (int8_t *)workspace;
     float *a_s = (float *)((uint8_t *)workspace + round_up((size_t)m * (size_t)k, 256));
-    hipError_t e = w4a8::launch_quantize_act(a, m, k, (int32_t)k, a_q, a_s, stream);
-    if (e != hipSuccess) return W4A8_ERR_HIP;
-    return finish(w4a8::launch_w4a8_gemm(a_q, a_s, w_packed, grp_scale, ch_scale, m, n, k, out,
-                                         (int)out_dtype, stream),
+    return finish(w4a8::launch_w4a8_gemm_bf16act(a, w_packed, grp_scale, ch_scale, m, n, k, out,
+                                                 (int)out_dtype, a_q, a_s, stream),
                   stream);
 }
 

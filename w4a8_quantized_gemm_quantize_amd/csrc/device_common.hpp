@@ -31,6 +31,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Every binary32 product and sum below must round on its own: no contraction
+// into fused multiply-adds (the build also passes -ffp-contract=off).
+#pragma clang fp contract(off)
+
 namespace w4a8 {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -64,6 +68,55 @@ __device__ __forceinline__ int sat_rne_code(float v, float lim) {
     return (int)r;
 }
 
+// 8 floats times inv -> 8 int8 codes rne(x * inv), little-endian in two words.
+// With a finite inverse, |x * inv| <= 127 (1 + 2^-24)^2 < 127.5.  Adding
+// 1.5 * 2^23 to the rounded product lands in [2^23, 2^24), where binary32
+// spacing is 1, so the sum is 1.5 * 2^23 + rne(product) (ties to even, since
+// 1.5 * 2^23 is even) and the low byte of its bits is the two's-complement
+// code.  NaN products (0 * inf) give NaN sums whose low byte is 0.  An
+// infinite inverse (amax below about 2^-121) takes the saturating path.
+__device__ __forceinline__ u32x2 codes8(const float f[8], float inv) {
+    uint32_t t[8];
+    if (inv <= 3.40282347e38f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float v = f[i] * inv;
+            t[i] = __float_as_uint(v + 12582912.0f);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = (uint32_t)sat_rne_code(f[i] * inv, 127.0f);
+    }
+    const uint32_t lo = __builtin_amdgcn_perm(t[1], t[0], 0x0c0c0400u) |
+                        __builtin_amdgcn_perm(t[3], t[2], 0x04000c0cu);
+    const uint32_t hi = __builtin_amdgcn_perm(t[5], t[4], 0x0c0c0400u) |
+                        __builtin_amdgcn_perm(t[7], t[6], 0x04000c0cu);
+    return u32x2{lo, hi};
+}
+
+// 8 bf16 (one 16-byte vector) -> 8 floats (exact).
+__device__ __forceinline__ void bf16x8_to_f32(const u32x4 &v, float f[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
+__device__ __forceinline__ float absmax_f32x8(const float f[8]) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(f[i]));
+    return m;
+}
+
+// Activation block scale and inverse: s = amax / 127, inv = 127 / amax (0 if amax == 0).
+__device__ __forceinline__ void act_scale_pair(float amax, float &s, float &inv) {
+    s = amax / 127.0f;
+    inv = (amax > 0.0f) ? (127.0f / amax) : 0.0f;
+}
+
 // Rebuild 4 int8 weights q*s from a word of 4 nibbles (one per byte, low bits).
 // mul = s | s << 16, add = (128 - 8 s) * 0x01010101.
 __device__ __forceinline__ int dequant4(uint32_t nib, uint32_t mul, uint32_t add) {
@@ -94,6 +147,15 @@ __device__ __forceinline__ v4i unpack_step(uint32_t p0, uint32_t p1, uint32_t mu
 
 __device__ __forceinline__ v4i mfma16x16x64(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// global_load_lds_dwordx4: each lane copies 16 bytes from its own global address
+// to LDS at lds_block + 16 * lane (lds_block must be the same for the whole
+// wavefront).  Completion is tracked by vmcnt: wait before reading the block.
+typedef __attribute__((address_space(1))) void *global_vptr;
+typedef __attribute__((address_space(3))) void *lds_vptr;
+__device__ __forceinline__ void global_to_lds16(const void *src, void *lds_block) {
+    __builtin_amdgcn_global_load_lds((global_vptr)src, (lds_vptr)lds_block, 16, 0, 0);
 }
 
 // Byte offset of chunk j of n-tile t in the packed weights.

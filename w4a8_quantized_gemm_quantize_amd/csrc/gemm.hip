@@ -1,5 +1,5 @@
 // gemm.hip -- W4A8 GEMM for gfx950: int8 activations x packed 4-bit weights,
-// int8 MFMA with exact int32 accumulation, per-group integer scales folded into
+// int8 MFMA with exact int32 accumulation, integer group scales folded into
 // the int8 weight operand, binary32 / bf16 / int32 epilogue.
 //
 // Method: "LiquidGEMM" verdict page (pith.science arXiv 2509.01229),
@@ -8,246 +8,589 @@
 // -- the rebuild is (u * s + a) XOR 0x80, one multiply-add and one XOR per four
 // weights (device_common.hpp: dequant4).  Because the group scale is a small
 // integer it is folded into the operand (q * s in [-112, 112] is still int8),
-// so acc = sum_g s_g * P_g comes out of the MFMA directly with no per-group
-// work on the accumulators.
+// so acc = sum_g s_g * P_g comes out of the MFMA with no per-group work on the
+// accumulators.  The same page's ImFP pipeline (pith_extraction.key_machinery:
+// loading, dequantization and MMA overlap) is realised here with LDS double
+// buffering (tiled kernel) and load batches issued ahead of use (skinny kernel).
 //
-// Two kernels:
-//   gemm_skinny_kernel  m <= 64 (decode shapes, HBM-bound): one workgroup per
-//                       16-channel tile, its wavefronts split K; weights stream
-//                       straight from HBM into registers in batches of chunks;
-//                       partial sums meet in LDS with integer adds (exact in any
-//                       order).
-//   gemm_tiled_kernel   m > 64 (prefill shapes, MFMA-bound): LDS-staged A and
-//                       packed W tiles, each wavefront unpacks its W fragments in
-//                       registers and issues v_mfma_i32_16x16x64_i8.
+// Operand roles on v_mfma_i32_16x16x64_i8: the rebuilt weights are operand A
+// (16 channels x 64 k; lane (c, kq) = c + 16 kq holds channel c, k = 16 kq ..
+// 16 kq + 15 -- exactly one record of the packed layout), the activations are
+// operand B (64 k x 16 rows; lane (r, kq) holds row r and the same 16 k).  The
+// result D[channel][row] arrives in lane (r, kq), element i = channel 4 kq + i:
+// four consecutive output columns of one output row per lane, stored as one
+// 8-byte (bf16) or 16-byte (fp32, int32) write.
 //
-// v_mfma_i32_16x16x64_i8 operand layout used throughout: lane l supplies
-// A[row = l % 16][k = 16 * (l / 16) .. +16] and B[k = 16 * (l / 16) .. +16][col =
-// l % 16] as 16 bytes each (A and B bytes pair position by position), and
-// receives D[row = 4 * (l / 16) + r][col = l % 16] in accumulator element r.
+// Kernels:
+//   gemm_skinny_kernel  m <= 64 (decode shapes, HBM-bound).  One workgroup per
+//                       NT 16-channel tiles; its wavefronts split K; packed
+//                       weights stream from HBM into registers, the next batch
+//                       of chunks requested before the current one is used.
+//                       Partial sums meet in LDS with integer adds (exact in any
+//                       order).  The FUSED form takes bf16 activations and
+//                       quantizes them per row into LDS (same codes8 rounding
+//                       as quantize_act_blockwise) while the first weight batch
+//                       is in flight.
+//   gemm_tiled_kernel   m > 64 (prefill shapes, MFMA-bound).  BM x BN tile per
+//                       workgroup of WAVES_M x WAVES_N wavefronts (256 x 256 as
+//                       2 x 4 wavefronts of 128 x 64);
+//                       activations, packed weights and per-group unpack
+//                       constants are staged in double-buffered LDS, one K chunk
+//                       (128) per barrier; each wavefront unpacks its weight
+//                       fragments in registers and reuses each one for
+//                       BM / (16 WAVES_M) MFMAs.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace w4a8 {
 namespace {
 
-__device__ __forceinline__ void store_out(void *out, int out_dtype, int64_t idx, int acc,
-                                          float sa, float sc) {
+// Epilogue for channels n..n+3 of output row `row` (n % 4 == 0).
+__device__ __forceinline__ void store4(void *out, int out_dtype, int64_t row, int64_t ldo,
+                                       int64_t n, v4i acc, float sa, f32x4 sc) {
+    const int64_t idx = row * ldo + n;
     if (out_dtype == 2) {
-        ((int *)out)[idx] = acc;
+        *(v4i *)((int *)out + idx) = acc;
         return;
     }
-    float y = (float)acc * sa;
-    y = y * sc;
-    if (out_dtype == 1)
-        ((uint16_t *)out)[idx] = (uint16_t)f32_to_bf16_rne(y);
-    else
-        ((float *)out)[idx] = y;
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        y[i] = (float)acc[i] * sa;
+        y[i] = y[i] * sc[i];
+    }
+    if (out_dtype == 1) {
+        const u32x2 b = {f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16),
+                         f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16)};
+        *(u32x2 *)((uint16_t *)out + idx) = b;
+    } else {
+        *(f32x4 *)((float *)out + idx) = f32x4{y[0], y[1], y[2], y[3]};
+    }
 }
 
 // ---------------------------------------------------------------- skinny --
-// MT = ceil(m / 16) row tiles (1..4), WAVES wavefronts split the K chunks,
-// D chunks per load batch.
-template <int MT, int WAVES, int D>
+constexpr int kSkinnyMaxVec = 16;   // fused prologue: 16-byte vectors held per thread
+
+template <int NT, int D, int MT, bool WITH_ACT>
+struct WeightBatch {
+    u32x4 w[D][NT];                       // one packed record per chunk and tile
+    uint32_t s[D][NT][2];                 // group scales of the chunk's two K steps
+    v4i a[WITH_ACT ? D : 1][2][MT];       // int8 activation fragments (non-fused)
+};
+
+template <int MT, int NT, int WAVES, int D, bool FUSED>
 __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
-    const int8_t *__restrict__ a_q, const float *__restrict__ a_scale,
+    const void *__restrict__ act, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ w_packed, const uint8_t *__restrict__ grp_scale,
-    const float *__restrict__ ch_scale, int m, int64_t n, int64_t k, void *__restrict__ out,
-    int out_dtype) {
-    __shared__ int red[MT * 16][16];
+    const float *__restrict__ ch_scale, int m, int64_t n, int64_t k,
+    void *__restrict__ out, int out_dtype, int8_t *__restrict__ ws_q,
+    float *__restrict__ ws_s) {
+    constexpr int THREADS = 64 * WAVES;
+    constexpr int ROWS = MT * 16;
+    extern __shared__ __attribute__((aligned(16))) uint8_t act_lds[];  // FUSED: [m][k + 16]
+    __shared__ int red[NT][16][ROWS + 4];
+    __shared__ float inv_lds[ROWS];
+    __shared__ float sa_lds[ROWS];
+    __shared__ unsigned amax_lds[ROWS];
+
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int c = lane & 15, kq = lane >> 4;
-    const int64_t t = blockIdx.x;
+    const int64_t ntiles = n / kNTile;
+    const int64_t t0 = (int64_t)blockIdx.x * NT;
     const int64_t nchunks = (k + kChunkK - 1) / kChunkK;
     const int64_t G = k / kGroup;
-    const uint8_t *tile = w_packed + t * kNTile * k / 2;
-    const uint8_t *sg = grp_scale + t * kNTile * G + c;
+    const int64_t lds_stride = k + 16;
 
-    for (int i = tid; i < MT * 16 * 16; i += 64 * WAVES) (&red[0][0])[i] = 0;
+    for (int i = tid; i < NT * 16 * (ROWS + 4); i += THREADS) (&red[0][0][0])[i] = 0;
+    if (tid < ROWS) amax_lds[tid] = 0u;
 
-    const int64_t per = (nchunks + WAVES - 1) / WAVES;
+    // Full 128-wide chunks are split evenly over the wavefronts; a trailing
+    // 64-wide chunk (k % 128 == 64) is done by the last wavefront afterwards, so
+    // the batched loads below carry no data-dependent branches.
+    const int64_t nfull = k / kChunkK;
+    const bool has_half = nfull < nchunks;
+    const int64_t per = (nfull + WAVES - 1) / WAVES;
     const int64_t j0 = wave * per;
-    const int64_t j1 = (j0 + per < nchunks) ? j0 + per : nchunks;
+    const int64_t j1 = (j0 + per < nfull) ? j0 + per : nfull;
+    const int8_t *a_q = (const int8_t *)act;
 
-    v4i acc[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = v4i{0, 0, 0, 0};
-
-    for (int64_t jb = j0; jb < j1; jb += D) {
-        u32x4 braw[D];
-        uint32_t sv[D][2];
-        v4i av[D][2][MT];
+    // Weights (+ non-fused activation fragments) of D chunks, requested together.
+    auto load_batch = [&](WeightBatch<NT, D, MT, !FUSED> &b, int64_t jb) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int64_t j = jb + d;
-            braw[d] = u32x4{0u, 0u, 0u, 0u};
-            sv[d][0] = sv[d][1] = 1u;
-            if (j < j1) {
-                const bool full = (j + 1) * kChunkK <= k;
-                if (full) {
-                    braw[d] = __builtin_nontemporal_load((const u32x4 *)(tile + j * kChunkBytes) + lane);
-                    sv[d][1] = sg[(2 * j + 1) * kNTile];
-                } else {
-                    u32x2 h = *((const u32x2 *)(tile + j * kChunkBytes) + lane);
-                    braw[d].x = h.x;
-                    braw[d].y = h.y;
+            const bool jv = j < j1;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int64_t t = t0 + nt;
+                b.w[d][nt] = u32x4{0u, 0u, 0u, 0u};
+                b.s[d][nt][0] = b.s[d][nt][1] = 1u;
+                if (jv && t < ntiles) {
+                    const uint8_t *sg = grp_scale + t * kNTile * G + (2 * j) * kNTile + c;
+                    b.w[d][nt] = __builtin_nontemporal_load(
+                        (const u32x4 *)(w_packed + packed_chunk_offset(t, j, k)) + lane);
+                    b.s[d][nt][0] = sg[0];
+                    b.s[d][nt][1] = sg[kNTile];
                 }
-                sv[d][0] = sg[(2 * j) * kNTile];
             }
+            if constexpr (!FUSED) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+                for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const int row = mt * 16 + c;
-                    const int64_t kk = j * kChunkK + h * kGroup + kq * 16;
-                    av[d][h][mt] = v4i{0, 0, 0, 0};
-                    if (j < j1 && row < m && kk < k)
-                        av[d][h][mt] = *(const v4i *)(a_q + (int64_t)row * k + kk);
-                }
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const int row = mt * 16 + c;
+                        b.a[d][h][mt] = v4i{0, 0, 0, 0};
+                        if (jv && row < m)
+                            b.a[d][h][mt] = *(const v4i *)(a_q + (int64_t)row * k + j * kChunkK +
+                                                           h * kGroup + kq * 16);
+                    }
+            }
         }
+    };
+
+    WeightBatch<NT, D, MT, !FUSED> cur;
+    load_batch(cur, j0);
+    __syncthreads();  // red / amax_lds cleared
+
+    if constexpr (FUSED) {
+        // Per-row absmax -> scale, then the row's codes into LDS.  Threads are
+        // split into m groups of tpr (a power of two) threads per row.  All
+        // loads are issued before any is used.
+        const u32x4 *a16 = (const u32x4 *)act;
+        const int64_t vpr = k / 8;
+        int tpr = THREADS;
+        while (tpr * m > THREADS) tpr >>= 1;
+        const int row = tid / tpr, sub = tid % tpr;
+        const bool row_ok = row < m;
+        u32x4 av[kSkinnyMaxVec];
+#pragma unroll
+        for (int u = 0; u < kSkinnyMaxVec; ++u) {
+            const int64_t v = sub + (int64_t)u * tpr;
+            av[u] = u32x4{0u, 0u, 0u, 0u};
+            if (row_ok && v < vpr) av[u] = a16[row * vpr + v];
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int u = 0; u < kSkinnyMaxVec; ++u) {
+            float f[8];
+            bf16x8_to_f32(av[u], f);
+            amax = __builtin_fmaxf(amax, absmax_f32x8(f));
+        }
+        const int span = tpr < 64 ? tpr : 64;
+        for (int off = 1; off < span; off <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
+        if (row_ok && (sub & (span - 1)) == 0) atomicMax(&amax_lds[row], __float_as_uint(amax));
+        __syncthreads();
+        if (tid < m) {
+            float s, inv;
+            act_scale_pair(__uint_as_float(amax_lds[tid]), s, inv);
+            inv_lds[tid] = inv;
+            sa_lds[tid] = s;
+            if (blockIdx.x == 0) ws_s[tid] = s;
+        }
+        __syncthreads();
+        if (row_ok) {
+            const float inv = inv_lds[row];
+#pragma unroll
+            for (int u = 0; u < kSkinnyMaxVec; ++u) {
+                const int64_t v = sub + (int64_t)u * tpr;
+                if (v < vpr) {
+                    float f[8];
+                    bf16x8_to_f32(av[u], f);
+                    const u32x2 q = codes8(f, inv);
+                    *(u32x2 *)(act_lds + row * lds_stride + v * 8) = q;
+                    if (blockIdx.x == 0) *(u32x2 *)(ws_q + row * k + v * 8) = q;
+                }
+            }
+        }
+        __syncthreads();
+    } else {
+        if (tid < m) sa_lds[tid] = a_scale[tid];
+        __syncthreads();
+    }
+
+    v4i acc[NT][MT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = v4i{0, 0, 0, 0};
+
+    // One K step (64) of one chunk: rebuild the weight operand of each tile and
+    // multiply it into every row tile.
+    auto mma_step = [&](const u32x2 wp[NT], const uint32_t sv[NT], const v4i av[MT]) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            uint32_t mul, add;
+            scale_consts(sv[nt], mul, add);
+            const v4i wv = unpack_step(wp[nt].x, wp[nt].y, mul, add);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = mfma16x16x64(wv, av[mt], acc[nt][mt]);
+        }
+    };
+    auto lds_act = [&](v4i av[MT], int64_t kk) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int row = mt * 16 + c;
+            av[mt] = v4i{0, 0, 0, 0};
+            if (row < m) av[mt] = *(const v4i *)(act_lds + row * lds_stride + kk);
+        }
+    };
+
+    for (int64_t jb = j0; jb < j1; jb += D) {
+        WeightBatch<NT, D, MT, !FUSED> nxt;
+        if (jb + D < j1) load_batch(nxt, jb + D);
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            if (jb + d < j1) {
+            const int64_t j = jb + d;
+            if (j >= j1) break;
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    uint32_t mul, add;
-                    scale_consts(sv[d][h], mul, add);
-                    const v4i b = unpack_step(h ? braw[d].z : braw[d].x,
-                                              h ? braw[d].w : braw[d].y, mul, add);
+            for (int h = 0; h < 2; ++h) {
+                u32x2 wp[NT];
+                uint32_t sv[NT];
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16x16x64(av[d][h][mt], b, acc[mt]);
+                for (int nt = 0; nt < NT; ++nt) {
+                    wp[nt] = h ? u32x2{cur.w[d][nt].z, cur.w[d][nt].w}
+                               : u32x2{cur.w[d][nt].x, cur.w[d][nt].y};
+                    sv[nt] = cur.s[d][nt][h];
                 }
+                v4i av[MT];
+                if constexpr (FUSED) {
+                    lds_act(av, j * kChunkK + h * kGroup + kq * 16);
+                } else {
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) av[mt] = cur.a[d][h][mt];
+                }
+                mma_step(wp, sv, av);
             }
         }
+        cur = nxt;
     }
-    __syncthreads();
+
+    if (has_half && wave == WAVES - 1) {
+        // Trailing 64-wide chunk: 8-byte lane records, one K step.
+        const int64_t j = nfull;
+        u32x2 wp[NT];
+        uint32_t sv[NT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) atomicAdd(&red[mt * 16 + 4 * kq + r][c], acc[mt][r]);
-    __syncthreads();
-    for (int i = tid; i < MT * 16 * 16; i += 64 * WAVES) {
-        const int row = i >> 4, col = i & 15;
-        if (row < m) {
-            const int64_t nn = t * kNTile + col;
-            store_out(out, out_dtype, (int64_t)row * n + nn, red[row][col], a_scale[row],
-                      ch_scale[nn]);
+        for (int nt = 0; nt < NT; ++nt) {
+            const int64_t t = t0 + nt;
+            wp[nt] = u32x2{0u, 0u};
+            sv[nt] = 1u;
+            if (t < ntiles) {
+                wp[nt] = *((const u32x2 *)(w_packed + packed_chunk_offset(t, j, k)) + lane);
+                sv[nt] = grp_scale[t * kNTile * G + (2 * j) * kNTile + c];
+            }
         }
+        v4i av[MT];
+        const int64_t kk = j * kChunkK + kq * 16;
+        if constexpr (FUSED) {
+            lds_act(av, kk);
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int row = mt * 16 + c;
+                av[mt] = v4i{0, 0, 0, 0};
+                if (row < m) av[mt] = *(const v4i *)(a_q + (int64_t)row * k + kk);
+            }
+        }
+        mma_step(wp, sv, av);
+    }
+
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) atomicAdd(&red[nt][4 * kq + i][mt * 16 + c], acc[nt][mt][i]);
+    __syncthreads();
+    for (int idx = tid; idx < NT * m * 4; idx += THREADS) {
+        const int nt = idx / (m * 4);
+        const int rem = idx - nt * m * 4;
+        const int row = rem >> 2, quad = rem & 3;
+        const int64_t t = t0 + nt;
+        if (t >= ntiles) continue;
+        const v4i a4 = {red[nt][4 * quad][row], red[nt][4 * quad + 1][row],
+                        red[nt][4 * quad + 2][row], red[nt][4 * quad + 3][row]};
+        const int64_t nn = t * kNTile + 4 * quad;
+        store4(out, out_dtype, row, n, nn, a4, sa_lds[row], *(const f32x4 *)(ch_scale + nn));
     }
 }
 
 // ----------------------------------------------------------------- tiled --
-// BM x BN output tile per 256-thread workgroup (2 x 2 wavefronts), one K chunk
-// (128) per iteration.  LDS: A tile [BM][128] int8 with the 16-byte column
-// index XOR-swizzled by (row % 8); W tile [BN/16][64 lanes][16 B] exactly as
-// packed; group scales [BN/16][2][16].
 template <int BM, int BN>
-__global__ __launch_bounds__(256) void gemm_tiled_kernel(
+struct TiledLds {
+    static constexpr int kAct = BM * kChunkK;            // [BM][128] int8, swizzled
+    static constexpr int kW = (BN / 16) * kChunkBytes;    // [BN/16][64][16] packed
+    static constexpr int kSc = (BN / 16) * 2 * 16 * 8;    // [BN/16][2][16] (mul, add)
+    static constexpr int kStage = kAct + kW + kSc;
+};
+
+// Byte offset of 16-byte column c16 (0..7) of activation row `row` in LDS: the
+// column index is XOR-swizzled so that 16 consecutive rows read at one logical
+// column hit distinct banks (for both 128- and 256-byte bank spans).
+__device__ __forceinline__ int act_lds_off(int row, int c16) {
+    return row * kChunkK + ((c16 ^ (row & 7) ^ ((row >> 3) & 1)) << 4);
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
     const int8_t *__restrict__ a_q, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ w_packed, const uint8_t *__restrict__ grp_scale,
     const float *__restrict__ ch_scale, int64_t m, int64_t n, int64_t k,
     void *__restrict__ out, int out_dtype) {
-    constexpr int WM = BM / 2, WN = BN / 2;
+    using L = TiledLds<BM, BN>;
+    constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int TM = WM / 16, TN = WN / 16;
-    constexpr int NT = BN / 16;
-    __shared__ __attribute__((aligned(16))) uint8_t a_lds[BM * kChunkK];
-    __shared__ __attribute__((aligned(16))) uint8_t b_lds[NT * kChunkBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t s_lds[NT * 2 * 16];
+    constexpr int NTB = BN / 16;                       // 16-channel tiles per block
+    constexpr int ACT_V = BM * 8 / THREADS;            // 16-byte act vectors per thread
+    constexpr int W_V = NTB * 64 / THREADS;            // 16-byte weight records per thread
+    constexpr int SC_T = NTB * 2 * 16 / 4;             // threads loading 4 group scales each
+    static_assert(ACT_V >= 1 && W_V >= 1 && SC_T <= THREADS, "tile shape");
+    static_assert(ACT_V * THREADS == BM * 8 && W_V * THREADS == NTB * 64, "tile shape");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::kStage];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     const int c = lane & 15, kq = lane >> 4;
+
+    // Tile order: consecutive workgroup ids are dispatched round-robin over the
+    // 8 XCDs; give each XCD a contiguous slice of a grouped (4 row tiles wide)
+    // traversal so the workgroups sharing an L2 share activation rows and
+    // weight columns.
     const int64_t mtiles = (m + BM - 1) / BM;
-    const int64_t bm = blockIdx.x % mtiles;
-    const int64_t bn = blockIdx.x / mtiles;
+    const int64_t ntb = (n + BN - 1) / BN;
+    const int64_t nwg = mtiles * ntb;
+    int64_t id = blockIdx.x;
+    if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
+    constexpr int64_t GM = 4;
+    const int64_t group = id / (GM * ntb);
+    const int64_t first_m = group * GM;
+    const int64_t gsize = (mtiles - first_m < GM) ? (mtiles - first_m) : GM;
+    const int64_t within = id - group * GM * ntb;
+    const int64_t bm = first_m + within % gsize;
+    const int64_t bn = within / gsize;
     const int64_t m0 = bm * BM, n0 = bn * BN;
     const int64_t t0 = n0 / kNTile;
     const int64_t ntiles = n / kNTile;
     const int64_t nchunks = (k + kChunkK - 1) / kChunkK;
     const int64_t G = k / kGroup;
 
-    v4i acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    u32x4 act_r[ACT_V];
+    u32x4 w_r[W_V];
+    uint32_t sc_r = 0x01010101u;
 
-    for (int64_t j = 0; j < nchunks; ++j) {
-        const bool full = (j + 1) * kChunkK <= k;
-        // global -> LDS: A
-        for (int idx = tid; idx < BM * 8; idx += 256) {
+    // Global -> registers for chunk j.  FULL chunks (the main loop) read 16-byte
+    // weight records and both group scales; the trailing 64-wide chunk reads
+    // 8-byte records and the first scale only.
+    auto load_global = [&](int64_t j, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+#pragma unroll
+        for (int i = 0; i < ACT_V; ++i) {
+            const int idx = i * THREADS + tid;
             const int row = idx >> 3, c16 = idx & 7;
             const int64_t gm = m0 + row;
-            const int64_t gk = j * kChunkK + c16 * 16;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (gm < m && gk < k) v = *(const uint4 *)(a_q + gm * k + gk);
-            *(uint4 *)(a_lds + row * kChunkK + ((c16 ^ (row & 7)) << 4)) = v;
+            act_r[i] = u32x4{0u, 0u, 0u, 0u};
+            if (gm < m && (FULL || c16 < 4))
+                act_r[i] = *(const u32x4 *)(a_q + gm * k + j * kChunkK + c16 * 16);
         }
-        // global -> LDS: packed W records
-        for (int idx = tid; idx < NT * 64; idx += 256) {
+#pragma unroll
+        for (int i = 0; i < W_V; ++i) {
+            const int idx = i * THREADS + tid;
             const int tt = idx >> 6, l = idx & 63;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            w_r[i] = u32x4{0u, 0u, 0u, 0u};
             if (t0 + tt < ntiles) {
                 const uint8_t *src = w_packed + packed_chunk_offset(t0 + tt, j, k);
-                if (full) {
-                    v = *((const uint4 *)src + l);
+                if constexpr (FULL) {
+                    w_r[i] = *((const u32x4 *)src + l);
                 } else {
-                    uint2 h = *((const uint2 *)src + l);
-                    v.x = h.x;
-                    v.y = h.y;
+                    const u32x2 h = *((const u32x2 *)src + l);
+                    w_r[i].x = h.x;
+                    w_r[i].y = h.y;
                 }
             }
-            *(uint4 *)(b_lds + tt * kChunkBytes + l * 16) = v;
         }
-        // group scales
-        for (int idx = tid; idx < NT * 2 * 16; idx += 256) {
-            const int tt = idx >> 5, h = (idx >> 4) & 1, cc = idx & 15;
-            uint8_t s = 1;
-            if (t0 + tt < ntiles && (h == 0 || full))
-                s = grp_scale[(t0 + tt) * kNTile * G + (2 * j + h) * kNTile + cc];
-            s_lds[idx] = s;
+        if (tid < SC_T) {
+            // 4 scales: tile tt, step h, channels 4 q .. 4 q + 3
+            const int tt = tid >> 3, h = (tid >> 2) & 1, q4 = tid & 3;
+            sc_r = 0x01010101u;
+            if (t0 + tt < ntiles && (FULL || h == 0))
+                sc_r = *(const uint32_t *)(grp_scale + (t0 + tt) * kNTile * G +
+                                           (2 * j + h) * kNTile + 4 * q4);
         }
-        __syncthreads();
+    };
+    auto store_lds = [&](int buf) {
+        uint8_t *base = lds + buf * L::kStage;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            if (h == 1 && !full) break;
-            v4i b[TN];
+        for (int i = 0; i < ACT_V; ++i) {
+            const int idx = i * THREADS + tid;
+            *(u32x4 *)(base + act_lds_off(idx >> 3, idx & 7)) = act_r[i];
+        }
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn) {
-                const int tt = wn * TN + tn;
-                const uint4 raw = *(const uint4 *)(b_lds + tt * kChunkBytes + lane * 16);
+        for (int i = 0; i < W_V; ++i) {
+            const int idx = i * THREADS + tid;
+            *(u32x4 *)(base + L::kAct + idx * 16) = w_r[i];
+        }
+        if (tid < SC_T) {
+            u32x2 *dst = (u32x2 *)(base + L::kAct + L::kW) + tid * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
                 uint32_t mul, add;
-                scale_consts(s_lds[tt * 32 + h * 16 + c], mul, add);
-                b[tn] = unpack_step(h ? raw.z : raw.x, h ? raw.w : raw.y, mul, add);
-            }
-#pragma unroll
-            for (int tm = 0; tm < TM; ++tm) {
-                const int row = wm * WM + tm * 16 + c;
-                const int c16 = h * 4 + kq;
-                const v4i a = *(const v4i *)(a_lds + row * kChunkK + ((c16 ^ (row & 7)) << 4));
-#pragma unroll
-                for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma16x16x64(a, b[tn], acc[tm][tn]);
+                scale_consts((sc_r >> (8 * e)) & 0xffu, mul, add);
+                dst[e] = u32x2{mul, add};
             }
         }
-        __syncthreads();
-    }
+    };
 
-    // Epilogue straight from the accumulator layout.
+    v4i acc[TN][TM];
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+    // One K step from LDS stage `base`: all LDS reads of the step first, then
+    // unpack each weight tile and multiply it into the wavefront's row tiles.
+    auto compute_step = [&](const uint8_t *base, int h) {
+        v4i av[TM];
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+            av[tm] = *(const v4i *)(base + act_lds_off(wm * WM + tm * 16 + c, h * 4 + kq));
+        u32x2 raw[TN];
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+            raw[tn] = *(const u32x2 *)(base + L::kAct + (wn * TN + tn) * kChunkBytes + lane * 16 +
+                                       h * 8);
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
-            const int64_t col = n0 + wn * WN + tn * 16 + c;
-            if (col >= n) continue;
-            const float sc = ch_scale[col];
+            const int tt = wn * TN + tn;
+            const u32x2 ma = *(const u32x2 *)(base + L::kAct + L::kW + ((tt * 2 + h) * 16 + c) * 8);
+            const v4i wv = unpack_step(raw[tn].x, raw[tn].y, ma.x, ma.y);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t row = m0 + wm * WM + tm * 16 + 4 * kq + r;
-                if (row < m) store_out(out, out_dtype, row * n + col, acc[tm][tn][r], a_scale[row], sc);
+            for (int tm = 0; tm < TM; ++tm) acc[tn][tm] = mfma16x16x64(wv, av[tm], acc[tn][tm]);
+        }
+    };
+
+    // Full chunks go global -> LDS directly (global_load_lds_dwordx4: lane l of
+    // the issuing wavefront writes 16 bytes at the LDS base + 16 l), so no VGPRs
+    // or ds_writes are spent on staging.  Each wavefront instruction fills one
+    // 1 KB block: 8 activation rows (lane -> row r0 + l / 8, swizzled column
+    // l % 8) or one 16-channel weight tile (lane -> record l).  Rows past m and
+    // tiles past n are clamped to valid addresses; their values only reach
+    // outputs that are never stored.
+    constexpr int WAVES = WAVES_M * WAVES_N;
+    auto issue_direct = [&](int64_t j, int buf) {
+        uint8_t *base = lds + buf * L::kStage;
+#pragma unroll
+        for (int i = 0; i < ACT_V; ++i) {
+            const int blk = i * WAVES + wave;
+            const int row = blk * 8 + (lane >> 3);
+            const int c16 = (lane & 7) ^ (row & 7) ^ ((row >> 3) & 1);
+            const int64_t gm = (m0 + row < m) ? m0 + row : m - 1;
+            global_to_lds16(a_q + gm * k + j * kChunkK + c16 * 16, base + blk * 1024);
+        }
+#pragma unroll
+        for (int i = 0; i < W_V; ++i) {
+            const int tt = i * WAVES + wave;
+            const int64_t t = (t0 + tt < ntiles) ? t0 + tt : ntiles - 1;
+            global_to_lds16(w_packed + packed_chunk_offset(t, j, k) + lane * 16,
+                            base + L::kAct + tt * kChunkBytes);
+        }
+        if (tid < SC_T) {
+            const int tt = tid >> 3, h = (tid >> 2) & 1, q4 = tid & 3;
+            sc_r = 0x01010101u;
+            if (t0 + tt < ntiles)
+                sc_r = *(const uint32_t *)(grp_scale + (t0 + tt) * kNTile * G +
+                                           (2 * j + h) * kNTile + 4 * q4);
+        }
+    };
+    auto store_sc = [&](int buf) {
+        if (tid < SC_T) {
+            u32x2 *dst = (u32x2 *)(lds + buf * L::kStage + L::kAct + L::kW) + tid * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t mul, add;
+                scale_consts((sc_r >> (8 * e)) & 0xffu, mul, add);
+                dst[e] = u32x2{mul, add};
             }
         }
+    };
+
+    const int64_t nfull = k / kChunkK;
+    if (nfull > 0) {
+        issue_direct(0, 0);
+        store_sc(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int64_t j = 0; j < nfull; ++j) {
+        const int buf = (int)(j & 1);
+        // buffer buf ^ 1 was last read before the previous barrier
+        if (j + 1 < nfull) issue_direct(j + 1, buf ^ 1);
+        const uint8_t *base = lds + buf * L::kStage;
+        compute_step(base, 0);
+        compute_step(base, 1);
+        if (j + 1 < nfull) store_sc(buf ^ 1);
+        __builtin_amdgcn_s_waitcnt(0);   // direct loads of the next chunk have landed
+        __syncthreads();
+    }
+    if (nfull * kChunkK < k) {
+        // trailing 64-wide chunk (k % 128 == 64), staged through registers
+        const std::integral_constant<bool, false> half_chunk;
+        load_global(nfull, half_chunk);
+        store_lds(0);
+        __syncthreads();
+        compute_step(lds, 0);
+    }
+
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+        const int64_t nn = n0 + wn * WN + tn * 16 + 4 * kq;
+        if (nn >= n) continue;
+        const f32x4 sc = *(const f32x4 *)(ch_scale + nn);
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+            const int64_t row = m0 + wm * WM + tm * 16 + c;
+            if (row < m) store4(out, out_dtype, row, n, nn, acc[tn][tm], a_scale[row], sc);
+        }
+    }
+}
+
+template <int MT, int NT, bool FUSED>
+void launch_skinny(const void *act, const float *a_scale, const uint8_t *w_packed,
+                   const uint8_t *grp_scale, const float *ch_scale, int64_t m, int64_t n,
+                   int64_t k, void *out, int out_dtype, int8_t *ws_q, float *ws_s,
+                   size_t dyn_lds, hipStream_t stream) {
+    // chunks per load batch: fewer when each batch also carries MT activation tiles
+    constexpr int WAVES = 8, D = FUSED ? 4 : (MT == 1 ? 4 : (MT == 2 ? 2 : 1));
+    const int64_t ntiles = n / kNTile;
+    const unsigned grid = (unsigned)((ntiles + NT - 1) / NT);
+    gemm_skinny_kernel<MT, NT, WAVES, D, FUSED><<<grid, 64 * WAVES, dyn_lds, stream>>>(
+        act, a_scale, w_packed, grp_scale, ch_scale, (int)m, n, k, out, out_dtype, ws_q, ws_s);
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+void launch_tiled(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
+                  const uint8_t *grp_scale, const float *ch_scale, int64_t m, int64_t n,
+                  int64_t k, void *out, int out_dtype, hipStream_t stream) {
+    const int64_t grid = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+    gemm_tiled_kernel<BM, BN, WAVES_M, WAVES_N><<<(unsigned)grid, 64 * WAVES_M * WAVES_N, 0,
+                                                  stream>>>(
+        a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out, out_dtype);
+}
+
+// Largest m * (k + 16) the fused skinny prologue keeps in LDS, and the vectors
+// per thread it holds in registers.
+constexpr int64_t kFusedLdsMax = 48 * 1024;
+
+bool fused_fits(int64_t m, int64_t k) {
+    if (m < 1 || m > 16 || k <= 0) return false;
+    if (m * (k + 16) > kFusedLdsMax) return false;
+    int64_t tpr = 512;
+    while (tpr * m > 512) tpr >>= 1;
+    return (k / 8 + tpr - 1) / tpr <= kSkinnyMaxVec;
 }
 
 }  // namespace
@@ -258,34 +601,43 @@ hipError_t launch_w4a8_gemm(const int8_t *a_q, const float *a_scale, const uint8
                             hipStream_t stream) {
     if (m == 0 || n == 0) return hipSuccess;
     const int64_t ntiles = n / kNTile;
-    if (m <= 64) {
-        const int mt = (int)((m + 15) / 16);
-        constexpr int W = 8, D = 4;
-        switch (mt) {
-            case 1:
-                gemm_skinny_kernel<1, W, D><<<(unsigned)ntiles, 64 * W, 0, stream>>>(
-                    a_q, a_scale, w_packed, grp_scale, ch_scale, (int)m, n, k, out, out_dtype);
-                break;
-            case 2:
-                gemm_skinny_kernel<2, W, D><<<(unsigned)ntiles, 64 * W, 0, stream>>>(
-                    a_q, a_scale, w_packed, grp_scale, ch_scale, (int)m, n, k, out, out_dtype);
-                break;
-            case 3:
-                gemm_skinny_kernel<3, W, 2><<<(unsigned)ntiles, 64 * W, 0, stream>>>(
-                    a_q, a_scale, w_packed, grp_scale, ch_scale, (int)m, n, k, out, out_dtype);
-                break;
-            default:
-                gemm_skinny_kernel<4, W, 2><<<(unsigned)ntiles, 64 * W, 0, stream>>>(
-                    a_q, a_scale, w_packed, grp_scale, ch_scale, (int)m, n, k, out, out_dtype);
-                break;
-        }
+    if (m <= 16) {
+        launch_skinny<1, 1, false>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out,
+                                   out_dtype, nullptr, nullptr, 0, stream);
+    } else if (m <= 32) {
+        launch_skinny<2, 1, false>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out,
+                                   out_dtype, nullptr, nullptr, 0, stream);
+    } else if (m <= 64) {
+        if (ntiles >= 512)
+            launch_skinny<4, 2, false>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k,
+                                       out, out_dtype, nullptr, nullptr, 0, stream);
+        else
+            launch_skinny<4, 1, false>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k,
+                                       out, out_dtype, nullptr, nullptr, 0, stream);
+    } else if (m <= 128) {
+        launch_tiled<128, 128, 2, 2>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out,
+                               out_dtype, stream);
     } else {
-        constexpr int BM = 128, BN = 128;
-        const int64_t grid = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-        gemm_tiled_kernel<BM, BN><<<(unsigned)grid, 256, 0, stream>>>(
-            a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out, out_dtype);
+        launch_tiled<256, 256, 2, 4>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out,
+                               out_dtype, stream);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_w4a8_gemm_bf16act(const uint16_t *a, const uint8_t *w_packed,
+                                    const uint8_t *grp_scale, const float *ch_scale, int64_t m,
+                                    int64_t n, int64_t k, void *out, int out_dtype,
+                                    int8_t *ws_q, float *ws_s, hipStream_t stream) {
+    if (m == 0 || n == 0) return hipSuccess;
+    if (fused_fits(m, k)) {
+        launch_skinny<1, 1, true>(a, nullptr, w_packed, grp_scale, ch_scale, m, n, k, out,
+                                  out_dtype, ws_q, ws_s, (size_t)(m * (k + 16)), stream);
+        return hipGetLastError();
+    }
+    hipError_t e = launch_quantize_act(a, m, k, (int32_t)k, ws_q, ws_s, stream);
+    if (e != hipSuccess) return e;
+    return launch_w4a8_gemm(ws_q, ws_s, w_packed, grp_scale, ch_scale, m, n, k, out, out_dtype,
+                            stream);
 }
 
 }  // namespace w4a8

@@ -19,5 +19,11 @@ hipError_t launch_unpack_w4(const uint8_t *w_packed, const uint8_t *grp_scale, i
 hipError_t launch_w4a8_gemm(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
                             const uint8_t *grp_scale, const float *ch_scale, int64_t m,
                             int64_t n, int64_t k, void *out, int out_dtype, hipStream_t stream);
+// Per-token quantization of bf16 activations into (ws_q, ws_s) and the GEMM;
+// small m runs both in one kernel.
+hipError_t launch_w4a8_gemm_bf16act(const uint16_t *a, const uint8_t *w_packed,
+                                    const uint8_t *grp_scale, const float *ch_scale, int64_t m,
+                                    int64_t n, int64_t k, void *out, int out_dtype,
+                                    int8_t *ws_q, float *ws_s, hipStream_t stream);
 
 }  // namespace w4a8

@@ -19,39 +19,6 @@
 namespace w4a8 {
 namespace {
 
-// 8 bf16 (one 16-byte load) -> 8 floats.
-__device__ __forceinline__ void load8(const u32x4 &v, float f[8]) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[2 * i] = __uint_as_float(w[i] << 16);
-        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-}
-
-__device__ __forceinline__ float absmax8(const float f[8]) {
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(f[i]));
-    return m;
-}
-
-// 8 floats * inv -> 8 int8 codes packed little-endian in two words.
-__device__ __forceinline__ u32x2 codes8(const float f[8], float inv) {
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        int c = sat_rne_code(f[i] * inv, 127.0f);
-        w[i >> 2] |= ((uint32_t)c & 0xffu) << (8 * (i & 3));
-    }
-    return u32x2{w[0], w[1]};
-}
-
-__device__ __forceinline__ void scale_pair(float amax, float &s, float &inv) {
-    s = amax / 127.0f;
-    inv = (amax > 0.0f) ? (127.0f / amax) : 0.0f;
-}
-
 // Blocks of 8 * LPB elements (LPB = 1..64 lanes, a power of two).  The tensor
 // is a flat sequence of blocks (cols % block == 0), so thread i owns the
 // 16-byte vector i and the LPB lanes of one block are adjacent in a wavefront.
@@ -74,13 +41,13 @@ __global__ __launch_bounds__(256) void quant_pow2_kernel(const u32x4 *__restrict
             // nvec is a multiple of LPB, so a block's lanes agree on this branch.
             if (idx < nvec) {
                 float f[8];
-                load8(v[u], f);
-                float amax = absmax8(f);
+                bf16x8_to_f32(v[u], f);
+                float amax = absmax_f32x8(f);
 #pragma unroll
                 for (int off = 1; off < LPB; off <<= 1)
                     amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
                 float s, inv;
-                scale_pair(amax, s, inv);
+                act_scale_pair(amax, s, inv);
                 q[idx] = codes8(f, inv);
                 if ((idx & (LPB - 1)) == 0) scales[idx / LPB] = s;
             }
@@ -108,14 +75,14 @@ __global__ __launch_bounds__(256) void quant_wide_kernel(const u32x4 *__restrict
             if (idx < block_vecs) {
                 v[u] = x[base + idx];
                 float f[8];
-                load8(v[u], f);
-                amax = __builtin_fmaxf(amax, absmax8(f));
+                bf16x8_to_f32(v[u], f);
+                amax = __builtin_fmaxf(amax, absmax_f32x8(f));
             }
         }
         for (int64_t idx = tid + (int64_t)MAXV * 256; idx < block_vecs; idx += 256) {
             float f[8];
-            load8(x[base + idx], f);
-            amax = __builtin_fmaxf(amax, absmax8(f));
+            bf16x8_to_f32(x[base + idx], f);
+            amax = __builtin_fmaxf(amax, absmax_f32x8(f));
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
@@ -124,19 +91,19 @@ __global__ __launch_bounds__(256) void quant_wide_kernel(const u32x4 *__restrict
         amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
         __syncthreads();
         float s, inv;
-        scale_pair(amax, s, inv);
+        act_scale_pair(amax, s, inv);
 #pragma unroll
         for (int u = 0; u < MAXV; ++u) {
             int64_t idx = tid + (int64_t)u * 256;
             if (idx < block_vecs) {
                 float f[8];
-                load8(v[u], f);
+                bf16x8_to_f32(v[u], f);
                 q[base + idx] = codes8(f, inv);
             }
         }
         for (int64_t idx = tid + (int64_t)MAXV * 256; idx < block_vecs; idx += 256) {
             float f[8];
-            load8(x[base + idx], f);
+            bf16x8_to_f32(x[base + idx], f);
             q[base + idx] = codes8(f, inv);
         }
         if (tid == 0) scales[b] = s;
