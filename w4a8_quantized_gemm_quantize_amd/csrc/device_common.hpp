@@ -117,6 +117,19 @@ __device__ __forceinline__ void act_scale_pair(float amax, float &s, float &inv)
     inv = (amax > 0.0f) ? (127.0f / amax) : 0.0f;
 }
 
+// Maximum of a non-negative 32-bit value over the 64 lanes of a wavefront with
+// DPP row operations (quad swaps, half-row and row mirrors, then row broadcasts
+// into rows 1-3); lane 63 ends with the total, which is returned to all lanes.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Rebuild 4 int8 weights q*s from a word of 4 nibbles (one per byte, low bits).
 // mul = s | s << 16, add = (128 - 8 s) * 0x01010101.
 __device__ __forceinline__ int dequant4(uint32_t nib, uint32_t mul, uint32_t add) {

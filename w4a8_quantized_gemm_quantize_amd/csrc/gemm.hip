@@ -80,7 +80,8 @@ struct WeightBatch {
     v4i a[WITH_ACT ? D : 1][2][MT];       // int8 activation fragments (non-fused)
 };
 
-template <int MT, int NT, int WAVES, int D, bool FUSED>
+// AV: 16-byte activation vectors per thread in the fused prologue (unused otherwise).
+template <int MT, int NT, int WAVES, int D, bool FUSED, int AV>
 __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     const void *__restrict__ act, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ w_packed, const uint8_t *__restrict__ grp_scale,
@@ -91,7 +92,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     constexpr int ROWS = MT * 16;
     extern __shared__ __attribute__((aligned(16))) uint8_t act_lds[];  // FUSED: [m][k + 16]
     __shared__ int red[NT][16][ROWS + 4];
-    __shared__ float inv_lds[ROWS];
     __shared__ float sa_lds[ROWS];
     __shared__ unsigned amax_lds[ROWS];
 
@@ -118,44 +118,42 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     const int8_t *a_q = (const int8_t *)act;
 
     // Weights (+ non-fused activation fragments) of D chunks, requested together.
+    // Every load is unconditional: addresses of chunks past the wavefront's range,
+    // tiles past n and rows past m are clamped to valid ones, and what they fetch
+    // is never used (chunks are skipped, rows masked at use, tiles not stored).
+    // A branch around a load would make the compiler wait for it at the join.
+    const int64_t tlast = ntiles - 1;
     auto load_batch = [&](WeightBatch<NT, D, MT, !FUSED> &b, int64_t jb) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            const int64_t j = jb + d;
-            const bool jv = j < j1;
+            const int64_t j = (jb + d < j1) ? jb + d : j1 - 1;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                const int64_t t = t0 + nt;
-                b.w[d][nt] = u32x4{0u, 0u, 0u, 0u};
-                b.s[d][nt][0] = b.s[d][nt][1] = 1u;
-                if (jv && t < ntiles) {
-                    const uint8_t *sg = grp_scale + t * kNTile * G + (2 * j) * kNTile + c;
-                    b.w[d][nt] = __builtin_nontemporal_load(
-                        (const u32x4 *)(w_packed + packed_chunk_offset(t, j, k)) + lane);
-                    b.s[d][nt][0] = sg[0];
-                    b.s[d][nt][1] = sg[kNTile];
-                }
+                const int64_t t = (t0 + nt < ntiles) ? t0 + nt : tlast;
+                const uint8_t *sg = grp_scale + t * kNTile * G + (2 * j) * kNTile + c;
+                b.w[d][nt] = __builtin_nontemporal_load(
+                    (const u32x4 *)(w_packed + packed_chunk_offset(t, j, k)) + lane);
+                b.s[d][nt][0] = sg[0];
+                b.s[d][nt][1] = sg[kNTile];
             }
             if constexpr (!FUSED) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
-                        const int row = mt * 16 + c;
-                        b.a[d][h][mt] = v4i{0, 0, 0, 0};
-                        if (jv && row < m)
-                            b.a[d][h][mt] = *(const v4i *)(a_q + (int64_t)row * k + j * kChunkK +
-                                                           h * kGroup + kq * 16);
+                        const int row = (mt * 16 + c < m) ? mt * 16 + c : m - 1;
+                        b.a[d][h][mt] = *(const v4i *)(a_q + (int64_t)row * k + j * kChunkK +
+                                                       h * kGroup + kq * 16);
                     }
             }
         }
     };
 
     WeightBatch<NT, D, MT, !FUSED> cur;
-    load_batch(cur, j0);
-    __syncthreads();  // red / amax_lds cleared
-
-    if constexpr (FUSED) {
+    if constexpr (!FUSED) {
+        if (j0 < j1) load_batch(cur, j0);
+        __syncthreads();  // red cleared
+    } else {
         // Per-row absmax -> scale, then the row's codes into LDS.  Threads are
         // split into m groups of tpr (a power of two) threads per row.  All
         // loads are issued before any is used.
@@ -165,36 +163,60 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
         while (tpr * m > THREADS) tpr >>= 1;
         const int row = tid / tpr, sub = tid % tpr;
         const bool row_ok = row < m;
-        u32x4 av[kSkinnyMaxVec];
+        // Unconditional loads from clamped (valid) addresses; vectors outside the
+        // row are ignored below.
+        const int64_t rowc = row_ok ? row : m - 1;
+        u32x4 av[AV];
 #pragma unroll
-        for (int u = 0; u < kSkinnyMaxVec; ++u) {
+        for (int u = 0; u < AV; ++u) {
             const int64_t v = sub + (int64_t)u * tpr;
-            av[u] = u32x4{0u, 0u, 0u, 0u};
-            if (row_ok && v < vpr) av[u] = a16[row * vpr + v];
+            av[u] = a16[rowc * vpr + (v < vpr ? v : vpr - 1)];
         }
+        // The first weight batch is requested after the activations: loads
+        // complete in order, so waiting for the activations below does not wait
+        // for the weights, which stream in while the prologue runs.
+        if (j0 < j1) load_batch(cur, j0);
+        __syncthreads();  // red / amax_lds cleared
         float amax = 0.0f;
 #pragma unroll
-        for (int u = 0; u < kSkinnyMaxVec; ++u) {
+        for (int u = 0; u < AV; ++u) {
             float f[8];
             bf16x8_to_f32(av[u], f);
-            amax = __builtin_fmaxf(amax, absmax_f32x8(f));
+            const float mx = absmax_f32x8(f);
+            if (row_ok && sub + (int64_t)u * tpr < vpr) amax = __builtin_fmaxf(amax, mx);
         }
-        const int span = tpr < 64 ? tpr : 64;
-        for (int off = 1; off < span; off <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
-        if (row_ok && (sub & (span - 1)) == 0) atomicMax(&amax_lds[row], __float_as_uint(amax));
-        __syncthreads();
-        if (tid < m) {
-            float s, inv;
-            act_scale_pair(__uint_as_float(amax_lds[tid]), s, inv);
-            inv_lds[tid] = inv;
-            sa_lds[tid] = s;
-            if (blockIdx.x == 0) ws_s[tid] = s;
+        // amax >= 0 and never NaN, so its bits order like unsigned integers.
+        float inv;
+        if (tpr == 64) {
+            // One wavefront per row: reduce in registers, no barrier needed.
+            const float rmax = __uint_as_float(wave_max_u32(__float_as_uint(amax)));
+            float s;
+            act_scale_pair(rmax, s, inv);
+            if (row_ok && lane == 0) {
+                sa_lds[row] = s;
+                if (blockIdx.x == 0) ws_s[row] = s;
+            }
+        } else {
+            // Rows spread over several wavefronts (tpr > 64) or share one (tpr < 64).
+            if (tpr > 64) {
+                const uint32_t wm = wave_max_u32(__float_as_uint(amax));
+                if (row_ok && lane == 0) atomicMax(&amax_lds[row], wm);
+            } else {
+                for (int off = 1; off < tpr; off <<= 1)
+                    amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
+                if (row_ok && sub == 0) atomicMax(&amax_lds[row], __float_as_uint(amax));
+            }
+            __syncthreads();
+            float s;
+            act_scale_pair(__uint_as_float(amax_lds[row_ok ? row : 0]), s, inv);
+            if (row_ok && sub == 0) {
+                sa_lds[row] = s;
+                if (blockIdx.x == 0) ws_s[row] = s;
+            }
         }
-        __syncthreads();
         if (row_ok) {
-            const float inv = inv_lds[row];
 #pragma unroll
-            for (int u = 0; u < kSkinnyMaxVec; ++u) {
+            for (int u = 0; u < AV; ++u) {
                 const int64_t v = sub + (int64_t)u * tpr;
                 if (v < vpr) {
                     float f[8];
@@ -205,9 +227,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
                 }
             }
         }
-        __syncthreads();
-    } else {
-        if (tid < m) sa_lds[tid] = a_scale[tid];
         __syncthreads();
     }
 
@@ -229,12 +248,18 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
             for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = mfma16x16x64(wv, av[mt], acc[nt][mt]);
         }
     };
+    // Activation fragments of rows mt * 16 + c; rows past m read row m - 1 and
+    // are zeroed here.
+    auto mask_rows = [&](v4i av[MT]) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            if (mt * 16 + c >= m) av[mt] = v4i{0, 0, 0, 0};
+    };
     auto lds_act = [&](v4i av[MT], int64_t kk) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const int row = mt * 16 + c;
-            av[mt] = v4i{0, 0, 0, 0};
-            if (row < m) av[mt] = *(const v4i *)(act_lds + row * lds_stride + kk);
+            const int row = (mt * 16 + c < m) ? mt * 16 + c : m - 1;
+            av[mt] = *(const v4i *)(act_lds + row * lds_stride + kk);
         }
     };
 
@@ -262,6 +287,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) av[mt] = cur.a[d][h][mt];
                 }
+                mask_rows(av);
                 mma_step(wp, sv, av);
             }
         }
@@ -275,13 +301,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
         uint32_t sv[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const int64_t t = t0 + nt;
-            wp[nt] = u32x2{0u, 0u};
-            sv[nt] = 1u;
-            if (t < ntiles) {
-                wp[nt] = *((const u32x2 *)(w_packed + packed_chunk_offset(t, j, k)) + lane);
-                sv[nt] = grp_scale[t * kNTile * G + (2 * j) * kNTile + c];
-            }
+            const int64_t t = (t0 + nt < ntiles) ? t0 + nt : tlast;
+            wp[nt] = *((const u32x2 *)(w_packed + packed_chunk_offset(t, j, k)) + lane);
+            sv[nt] = grp_scale[t * kNTile * G + (2 * j) * kNTile + c];
         }
         v4i av[MT];
         const int64_t kk = j * kChunkK + kq * 16;
@@ -290,11 +312,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
         } else {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const int row = mt * 16 + c;
-                av[mt] = v4i{0, 0, 0, 0};
-                if (row < m) av[mt] = *(const v4i *)(a_q + (int64_t)row * k + kk);
+                const int row = (mt * 16 + c < m) ? mt * 16 + c : m - 1;
+                av[mt] = *(const v4i *)(a_q + (int64_t)row * k + kk);
             }
         }
+        mask_rows(av);
         mma_step(wp, sv, av);
     }
 
@@ -314,7 +336,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
         const v4i a4 = {red[nt][4 * quad][row], red[nt][4 * quad + 1][row],
                         red[nt][4 * quad + 2][row], red[nt][4 * quad + 3][row]};
         const int64_t nn = t * kNTile + 4 * quad;
-        store4(out, out_dtype, row, n, nn, a4, sa_lds[row], *(const f32x4 *)(ch_scale + nn));
+        const float sa = FUSED ? sa_lds[row] : a_scale[row];
+        store4(out, out_dtype, row, n, nn, a4, sa, *(const f32x4 *)(ch_scale + nn));
     }
 }
 
@@ -500,10 +523,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
         }
         if (tid < SC_T) {
             const int tt = tid >> 3, h = (tid >> 2) & 1, q4 = tid & 3;
-            sc_r = 0x01010101u;
-            if (t0 + tt < ntiles)
-                sc_r = *(const uint32_t *)(grp_scale + (t0 + tt) * kNTile * G +
-                                           (2 * j + h) * kNTile + 4 * q4);
+            const int64_t t = (t0 + tt < ntiles) ? t0 + tt : ntiles - 1;
+            sc_r = *(const uint32_t *)(grp_scale + t * kNTile * G + (2 * j + h) * kNTile + 4 * q4);
         }
     };
     auto store_sc = [&](int buf) {
@@ -558,7 +579,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
     }
 }
 
-template <int MT, int NT, bool FUSED>
+template <int MT, int NT, bool FUSED, int AV = 1>
 void launch_skinny(const void *act, const float *a_scale, const uint8_t *w_packed,
                    const uint8_t *grp_scale, const float *ch_scale, int64_t m, int64_t n,
                    int64_t k, void *out, int out_dtype, int8_t *ws_q, float *ws_s,
@@ -567,7 +588,7 @@ void launch_skinny(const void *act, const float *a_scale, const uint8_t *w_packe
     constexpr int WAVES = 8, D = FUSED ? 4 : (MT == 1 ? 4 : (MT == 2 ? 2 : 1));
     const int64_t ntiles = n / kNTile;
     const unsigned grid = (unsigned)((ntiles + NT - 1) / NT);
-    gemm_skinny_kernel<MT, NT, WAVES, D, FUSED><<<grid, 64 * WAVES, dyn_lds, stream>>>(
+    gemm_skinny_kernel<MT, NT, WAVES, D, FUSED, AV><<<grid, 64 * WAVES, dyn_lds, stream>>>(
         act, a_scale, w_packed, grp_scale, ch_scale, (int)m, n, k, out, out_dtype, ws_q, ws_s);
 }
 
@@ -585,12 +606,15 @@ void launch_tiled(const int8_t *a_q, const float *a_scale, const uint8_t *w_pack
 // per thread it holds in registers.
 constexpr int64_t kFusedLdsMax = 48 * 1024;
 
-bool fused_fits(int64_t m, int64_t k) {
-    if (m < 1 || m > 16 || k <= 0) return false;
-    if (m * (k + 16) > kFusedLdsMax) return false;
+// Activation vectors per thread the fused prologue needs for m rows of k
+// (0 if the fused form does not apply).
+int fused_vectors(int64_t m, int64_t k) {
+    if (m < 1 || m > 16 || k <= 0) return 0;
+    if (m * (k + 16) > kFusedLdsMax) return 0;
     int64_t tpr = 512;
     while (tpr * m > 512) tpr >>= 1;
-    return (k / 8 + tpr - 1) / tpr <= kSkinnyMaxVec;
+    const int64_t need = (k / 8 + tpr - 1) / tpr;
+    return need <= 4 ? 4 : need <= 8 ? 8 : need <= kSkinnyMaxVec ? 16 : 0;
 }
 
 }  // namespace
@@ -629,9 +653,18 @@ hipError_t launch_w4a8_gemm_bf16act(const uint16_t *a, const uint8_t *w_packed,
                                     int64_t n, int64_t k, void *out, int out_dtype,
                                     int8_t *ws_q, float *ws_s, hipStream_t stream) {
     if (m == 0 || n == 0) return hipSuccess;
-    if (fused_fits(m, k)) {
-        launch_skinny<1, 1, true>(a, nullptr, w_packed, grp_scale, ch_scale, m, n, k, out,
-                                  out_dtype, ws_q, ws_s, (size_t)(m * (k + 16)), stream);
+    const int av = fused_vectors(m, k);
+    if (av > 0) {
+        const size_t lds_bytes = (size_t)(m * (k + 16));
+        if (av == 4)
+            launch_skinny<1, 1, true, 4>(a, nullptr, w_packed, grp_scale, ch_scale, m, n, k, out,
+                                         out_dtype, ws_q, ws_s, lds_bytes, stream);
+        else if (av == 8)
+            launch_skinny<1, 1, true, 8>(a, nullptr, w_packed, grp_scale, ch_scale, m, n, k, out,
+                                         out_dtype, ws_q, ws_s, lds_bytes, stream);
+        else
+            launch_skinny<1, 1, true, 16>(a, nullptr, w_packed, grp_scale, ch_scale, m, n, k,
+                                          out, out_dtype, ws_q, ws_s, lds_bytes, stream);
         return hipGetLastError();
     }
     hipError_t e = launch_quantize_act(a, m, k, (int32_t)k, ws_q, ws_s, stream);
