@@ -162,6 +162,15 @@ __device__ __forceinline__ v4i mfma16x16x64(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// v_mfma_i32_32x32x32_i8: lane l supplies A[row l % 32][k 16 (l / 32) .. +16] and
+// B[k 16 (l / 32) .. +16][col l % 32]; result element r of lane l is
+// D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
+__device__ __forceinline__ v16i mfma32x32x32(v4i a, v4i b, v16i c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
 // global_load_lds_dwordx4: each lane copies 16 bytes from its own global address
 // to LDS at lds_block + 16 * lane (lds_block must be the same for the whole
 // wavefront).  Completion is tracked by vmcnt: wait before reading the block.

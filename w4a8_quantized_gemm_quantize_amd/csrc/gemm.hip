@@ -31,14 +31,12 @@
 //                       quantizes them per row into LDS (same codes8 rounding
 //                       as quantize_act_blockwise) while the first weight batch
 //                       is in flight.
-//   gemm_tiled_kernel   m > 64 (prefill shapes, MFMA-bound).  BM x BN tile per
-//                       workgroup of WAVES_M x WAVES_N wavefronts (256 x 256 as
-//                       2 x 4 wavefronts of 128 x 64);
-//                       activations, packed weights and per-group unpack
-//                       constants are staged in double-buffered LDS, one K chunk
-//                       (128) per barrier; each wavefront unpacks its weight
-//                       fragments in registers and reuses each one for
-//                       BM / (16 WAVES_M) MFMAs.
+//   gemm_tiled_kernel   m > 64 (prefill shapes, MFMA-bound).  256 x 256 tile per
+//                       workgroup of 16 wavefronts (64 x 64 each, four per
+//                       SIMD); activations (direct global -> LDS loads) and
+//                       rebuilt int8 weight operands in double-buffered LDS,
+//                       one K chunk (128) per barrier; each 16-channel weight
+//                       tile is rebuilt once per workgroup, by one wavefront.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -342,19 +340,32 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 }
 
 // ----------------------------------------------------------------- tiled --
+// BM x BN output tile per workgroup of WAVES_M x WAVES_N wavefronts, each
+// wavefront (BM / WAVES_M) x (BN / WAVES_N).  K advances one 128-wide chunk per
+// barrier through two LDS stages, each holding
+//   act: [BM][128] int8 activations (16-byte columns XOR-swizzled by row % 8),
+//   w:   [BN/16][2 steps][64 lanes][16 B] rebuilt int8 weight operands, each
+//        exactly the operand A of v_mfma_i32_16x16x64_i8 for 16 channels.
+// Weights are rebuilt once per workgroup, not once per wavefront: while the
+// workgroup multiplies chunk j, each wavefront fetches the packed records of
+// its own 16-channel tile(s) for chunk j + 1 straight into registers, rebuilds
+// them (unpack + group scale, device_common.hpp) and writes the int8 operands
+// into the other stage.  The MFMA loop itself is LDS reads and MFMAs only, and
+// small per-wavefront register budgets keep four wavefronts per SIMD so the
+// matrix cores always have work to issue.
 template <int BM, int BN>
 struct TiledLds {
-    static constexpr int kAct = BM * kChunkK;            // [BM][128] int8, swizzled
-    static constexpr int kW = (BN / 16) * kChunkBytes;    // [BN/16][64][16] packed
-    static constexpr int kSc = (BN / 16) * 2 * 16 * 8;    // [BN/16][2][16] (mul, add)
-    static constexpr int kStage = kAct + kW + kSc;
+    static constexpr int kAct = BM * kChunkK;                 // activations
+    static constexpr int kW = (BN / 16) * 2 * kChunkBytes;     // rebuilt weights
 };
 
-// Byte offset of 16-byte column c16 (0..7) of activation row `row` in LDS: the
-// column index is XOR-swizzled so that 16 consecutive rows read at one logical
-// column hit distinct banks (for both 128- and 256-byte bank spans).
+// Byte offset of 16-byte column c16 (0..7) of activation row `row` in LDS.  The
+// 16 x 16 x 64 MFMA operand read has 16 consecutive rows at one column per
+// 16-lane group; XOR-ing the column with row % 8 makes that ds_read_b128
+// conflict-free on gfx950 (measured with SQ_LDS_BANK_CONFLICT).
+__device__ __forceinline__ int act_swz(int row, int c16) { return c16 ^ (row & 7); }
 __device__ __forceinline__ int act_lds_off(int row, int c16) {
-    return row * kChunkK + ((c16 ^ (row & 7) ^ ((row >> 3) & 1)) << 4);
+    return row * kChunkK + (act_swz(row, c16) << 4);
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
@@ -364,26 +375,32 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
     const float *__restrict__ ch_scale, int64_t m, int64_t n, int64_t k,
     void *__restrict__ out, int out_dtype) {
     using L = TiledLds<BM, BN>;
-    constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+    constexpr int WAVES = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-    constexpr int TM = WM / 16, TN = WN / 16;
-    constexpr int NTB = BN / 16;                       // 16-channel tiles per block
-    constexpr int ACT_V = BM * 8 / THREADS;            // 16-byte act vectors per thread
-    constexpr int W_V = NTB * 64 / THREADS;            // 16-byte weight records per thread
-    constexpr int SC_T = NTB * 2 * 16 / 4;             // threads loading 4 group scales each
-    static_assert(ACT_V >= 1 && W_V >= 1 && SC_T <= THREADS, "tile shape");
-    static_assert(ACT_V * THREADS == BM * 8 && W_V * THREADS == NTB * 64, "tile shape");
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::kStage];
+    constexpr int TM = WM / 16, TN = WN / 16;   // 16 x 16 MFMA tiles per wavefront
+    constexpr int NTB = BN / 16;              // 16-channel tiles per workgroup
+    constexpr int TPW = NTB / WAVES;          // tiles each wavefront rebuilds
+    constexpr int ACT_I = BM / 8 / WAVES;     // 1 KB activation blocks per wavefront
+    static_assert(TPW >= 1 && TPW * WAVES == NTB, "one or more weight tiles per wavefront");
+    static_assert(ACT_I >= 1 && ACT_I * WAVES * 8 == BM, "activation blocks per wavefront");
+    // Each stage of each operand is its own array and the chunk loop is unrolled
+    // by two so every access names its array statically: the direct-to-LDS
+    // activation loads into one stage then provably never alias reads of the
+    // other stage or the weight writes, and the compiler does not make those
+    // wait for the loads in flight.
+    __shared__ __attribute__((aligned(16))) uint8_t act0[L::kAct];
+    __shared__ __attribute__((aligned(16))) uint8_t act1[L::kAct];
+    __shared__ __attribute__((aligned(16))) uint8_t wl0[L::kW];
+    __shared__ __attribute__((aligned(16))) uint8_t wl1[L::kW];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-    const int c = lane & 15, kq = lane >> 4;
+    const int c = lane & 15;
 
-    // Tile order: consecutive workgroup ids are dispatched round-robin over the
-    // 8 XCDs; give each XCD a contiguous slice of a grouped (4 row tiles wide)
-    // traversal so the workgroups sharing an L2 share activation rows and
-    // weight columns.
+    // Tile order: consecutive workgroup ids go round-robin over the 8 XCDs, so
+    // each XCD gets a contiguous slice of a grouped traversal (4 row tiles per
+    // group) and the workgroups sharing an L2 share activation rows and weights.
     const int64_t mtiles = (m + BM - 1) / BM;
     const int64_t ntb = (n + BN - 1) / BN;
     const int64_t nwg = mtiles * ntb;
@@ -394,76 +411,72 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
     const int64_t first_m = group * GM;
     const int64_t gsize = (mtiles - first_m < GM) ? (mtiles - first_m) : GM;
     const int64_t within = id - group * GM * ntb;
-    const int64_t bm = first_m + within % gsize;
-    const int64_t bn = within / gsize;
-    const int64_t m0 = bm * BM, n0 = bn * BN;
+    const int64_t m0 = (first_m + within % gsize) * BM;
+    const int64_t n0 = (within / gsize) * BN;
     const int64_t t0 = n0 / kNTile;
     const int64_t ntiles = n / kNTile;
     const int64_t nchunks = (k + kChunkK - 1) / kChunkK;
     const int64_t G = k / kGroup;
 
-    u32x4 act_r[ACT_V];
-    u32x4 w_r[W_V];
-    uint32_t sc_r = 0x01010101u;
-
-    // Global -> registers for chunk j.  FULL chunks (the main loop) read 16-byte
-    // weight records and both group scales; the trailing 64-wide chunk reads
-    // 8-byte records and the first scale only.
-    auto load_global = [&](int64_t j, auto full_tag) {
-        constexpr bool FULL = decltype(full_tag)::value;
+    // Activations of chunk j -> stage buf, global -> LDS directly
+    // (global_load_lds_dwordx4 fills one 1 KB block = 8 rows per instruction).
+    // Rows past m are clamped to row m - 1; they only reach unstored outputs.
+    // For the trailing 64-wide chunk the upper 64 columns are clamped into the
+    // row as well and never read.
+    auto issue_act = [&](int64_t j, auto buf_tag) {
+        uint8_t *base = decltype(buf_tag)::value ? act1 : act0;
+        const bool full = (j + 1) * kChunkK <= k;
 #pragma unroll
-        for (int i = 0; i < ACT_V; ++i) {
-            const int idx = i * THREADS + tid;
-            const int row = idx >> 3, c16 = idx & 7;
-            const int64_t gm = m0 + row;
-            act_r[i] = u32x4{0u, 0u, 0u, 0u};
-            if (gm < m && (FULL || c16 < 4))
-                act_r[i] = *(const u32x4 *)(a_q + gm * k + j * kChunkK + c16 * 16);
-        }
-#pragma unroll
-        for (int i = 0; i < W_V; ++i) {
-            const int idx = i * THREADS + tid;
-            const int tt = idx >> 6, l = idx & 63;
-            w_r[i] = u32x4{0u, 0u, 0u, 0u};
-            if (t0 + tt < ntiles) {
-                const uint8_t *src = w_packed + packed_chunk_offset(t0 + tt, j, k);
-                if constexpr (FULL) {
-                    w_r[i] = *((const u32x4 *)src + l);
-                } else {
-                    const u32x2 h = *((const u32x2 *)src + l);
-                    w_r[i].x = h.x;
-                    w_r[i].y = h.y;
-                }
-            }
-        }
-        if (tid < SC_T) {
-            // 4 scales: tile tt, step h, channels 4 q .. 4 q + 3
-            const int tt = tid >> 3, h = (tid >> 2) & 1, q4 = tid & 3;
-            sc_r = 0x01010101u;
-            if (t0 + tt < ntiles && (FULL || h == 0))
-                sc_r = *(const uint32_t *)(grp_scale + (t0 + tt) * kNTile * G +
-                                           (2 * j + h) * kNTile + 4 * q4);
+        for (int i = 0; i < ACT_I; ++i) {
+            const int blk = i * WAVES + wave;
+            const int row = blk * 8 + (lane >> 3);
+            int c16 = act_swz(row, lane & 7);   // the swizzle is its own inverse
+            if (!full) c16 &= 3;
+            const int64_t gm = (m0 + row < m) ? m0 + row : m - 1;
+            global_to_lds16(a_q + gm * k + j * kChunkK + c16 * 16, base + blk * 1024);
         }
     };
-    auto store_lds = [&](int buf) {
-        uint8_t *base = lds + buf * L::kStage;
+    // Packed records and group scales of this wavefront's tile(s) for chunk j:
+    // exactly three loads per tile whatever the chunk (the waits below count
+    // them).  Tiles past n are clamped to the last tile (outputs not stored).
+    // A trailing 64-wide chunk has 8-byte records: the 16-byte window is
+    // clamped inside the 512-byte chunk and the wanted half picked after the
+    // load; its missing second group reuses the first group's scale.
+    u32x4 wrec[TPW];
+    uint32_t wsc[TPW][2];
+    bool wfull = true;
+    auto fetch_w = [&](int64_t j) {
+        wfull = (j + 1) * kChunkK <= k;
+        const int rec_off = wfull ? lane * 16 : (lane * 8 < 496 ? lane * 8 : 496);
+        const int64_t g1 = wfull ? 2 * j + 1 : 2 * j;
 #pragma unroll
-        for (int i = 0; i < ACT_V; ++i) {
-            const int idx = i * THREADS + tid;
-            *(u32x4 *)(base + act_lds_off(idx >> 3, idx & 7)) = act_r[i];
+        for (int i = 0; i < TPW; ++i) {
+            const int64_t t = (t0 + wave * TPW + i < ntiles) ? t0 + wave * TPW + i : ntiles - 1;
+            const uint8_t *sg = grp_scale + t * kNTile * G + c;
+            wrec[i] = *(const u32x4 *)(w_packed + packed_chunk_offset(t, j, k) + rec_off);
+            wsc[i][0] = sg[(2 * j) * kNTile];
+            wsc[i][1] = sg[g1 * kNTile];
+        }
+    };
+    // Rebuild the int8 operands of both K steps into stage buf.
+    auto rebuild_w = [&](auto buf_tag) {
+        uint8_t *wbase = decltype(buf_tag)::value ? wl1 : wl0;
+        if (!wfull) {
+#pragma unroll
+            for (int i = 0; i < TPW; ++i)
+                wrec[i] = (lane == 63) ? u32x4{wrec[i].z, wrec[i].w, 0u, 0u}
+                                       : u32x4{wrec[i].x, wrec[i].y, 0u, 0u};
         }
 #pragma unroll
-        for (int i = 0; i < W_V; ++i) {
-            const int idx = i * THREADS + tid;
-            *(u32x4 *)(base + L::kAct + idx * 16) = w_r[i];
-        }
-        if (tid < SC_T) {
-            u32x2 *dst = (u32x2 *)(base + L::kAct + L::kW) + tid * 4;
+        for (int i = 0; i < TPW; ++i) {
+            const int tt = wave * TPW + i;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            for (int h = 0; h < 2; ++h) {
                 uint32_t mul, add;
-                scale_consts((sc_r >> (8 * e)) & 0xffu, mul, add);
-                dst[e] = u32x2{mul, add};
+                scale_consts(wsc[i][h], mul, add);
+                const v4i wv = unpack_step(h ? wrec[i].z : wrec[i].x, h ? wrec[i].w : wrec[i].y,
+                                           mul, add);
+                *(v4i *)(wbase + ((tt * 2 + h) * 64 + lane) * 16) = wv;
             }
         }
     };
@@ -472,103 +485,76 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
 #pragma unroll
     for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int j = 0; j < TM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+        for (int jj = 0; jj < TM; ++jj) acc[i][jj] = v4i{0, 0, 0, 0};
 
-    // One K step from LDS stage `base`: all LDS reads of the step first, then
-    // unpack each weight tile and multiply it into the wavefront's row tiles.
-    auto compute_step = [&](const uint8_t *base, int h) {
-        v4i av[TM];
+    // One K step (64) of stage buf: LDS reads and MFMAs only.  Activation
+    // fragment: lane (c, kq) reads row c of the row tile at 16-byte column
+    // 4 h + kq; weight fragments are stored in operand order.
+    const int kq = lane >> 4;
+    auto mma_step = [&](auto buf_tag, int h) {
+        const uint8_t *abase = decltype(buf_tag)::value ? act1 : act0;
+        const uint8_t *wbase = decltype(buf_tag)::value ? wl1 : wl0;
+        v4i av[TM], wv[TN];
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm)
-            av[tm] = *(const v4i *)(base + act_lds_off(wm * WM + tm * 16 + c, h * 4 + kq));
-        u32x2 raw[TN];
+            av[tm] = *(const v4i *)(abase + act_lds_off(wm * WM + tm * 16 + c, 4 * h + kq));
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
-            raw[tn] = *(const u32x2 *)(base + L::kAct + (wn * TN + tn) * kChunkBytes + lane * 16 +
-                                       h * 8);
+            wv[tn] = *(const v4i *)(wbase + (((wn * TN + tn) * 2 + h) * 64 + lane) * 16);
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-            const int tt = wn * TN + tn;
-            const u32x2 ma = *(const u32x2 *)(base + L::kAct + L::kW + ((tt * 2 + h) * 16 + c) * 8);
-            const v4i wv = unpack_step(raw[tn].x, raw[tn].y, ma.x, ma.y);
+        for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-            for (int tm = 0; tm < TM; ++tm) acc[tn][tm] = mfma16x16x64(wv, av[tm], acc[tn][tm]);
-        }
+            for (int tm = 0; tm < TM; ++tm) acc[tn][tm] = mfma16x16x64(wv[tn], av[tm], acc[tn][tm]);
     };
 
-    // Full chunks go global -> LDS directly (global_load_lds_dwordx4: lane l of
-    // the issuing wavefront writes 16 bytes at the LDS base + 16 l), so no VGPRs
-    // or ds_writes are spent on staging.  Each wavefront instruction fills one
-    // 1 KB block: 8 activation rows (lane -> row r0 + l / 8, swizzled column
-    // l % 8) or one 16-channel weight tile (lane -> record l).  Rows past m and
-    // tiles past n are clamped to valid addresses; their values only reach
-    // outputs that are never stored.
-    constexpr int WAVES = WAVES_M * WAVES_N;
-    auto issue_direct = [&](int64_t j, int buf) {
-        uint8_t *base = lds + buf * L::kStage;
-#pragma unroll
-        for (int i = 0; i < ACT_V; ++i) {
-            const int blk = i * WAVES + wave;
-            const int row = blk * 8 + (lane >> 3);
-            const int c16 = (lane & 7) ^ (row & 7) ^ ((row >> 3) & 1);
-            const int64_t gm = (m0 + row < m) ? m0 + row : m - 1;
-            global_to_lds16(a_q + gm * k + j * kChunkK + c16 * 16, base + blk * 1024);
-        }
-#pragma unroll
-        for (int i = 0; i < W_V; ++i) {
-            const int tt = i * WAVES + wave;
-            const int64_t t = (t0 + tt < ntiles) ? t0 + tt : ntiles - 1;
-            global_to_lds16(w_packed + packed_chunk_offset(t, j, k) + lane * 16,
-                            base + L::kAct + tt * kChunkBytes);
-        }
-        if (tid < SC_T) {
-            const int tt = tid >> 3, h = (tid >> 2) & 1, q4 = tid & 3;
-            const int64_t t = (t0 + tt < ntiles) ? t0 + tt : ntiles - 1;
-            sc_r = *(const uint32_t *)(grp_scale + t * kNTile * G + (2 * j + h) * kNTile + 4 * q4);
-        }
-    };
-    auto store_sc = [&](int buf) {
-        if (tid < SC_T) {
-            u32x2 *dst = (u32x2 *)(lds + buf * L::kStage + L::kAct + L::kW) + tid * 4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint32_t mul, add;
-                scale_consts((sc_r >> (8 * e)) & 0xffu, mul, add);
-                dst[e] = u32x2{mul, add};
-            }
-        }
-    };
+    // Workgroup barrier for the LDS stages: wait until this wavefront's LDS
+    // writes and vector-memory loads (including the direct-to-LDS ones) are
+    // done, then s_barrier.  The empty asm statements keep the compiler from
+    // moving memory accesses across it.
+#define W4A8_LDS_BARRIER()                                                               \
+    do {                                                                                \
+        __builtin_amdgcn_s_waitcnt(0);                                                  \
+        asm volatile("" ::: "memory");                                                  \
+        __builtin_amdgcn_s_barrier();                                                   \
+        asm volatile("" ::: "memory");                                                  \
+    } while (0)
 
-    const int64_t nfull = k / kChunkK;
-    if (nfull > 0) {
-        issue_direct(0, 0);
-        store_sc(0);
+    // Pipeline over K chunks: iteration j multiplies stage `cur` while stage
+    // `nxt` is filled for chunk j + 1.  Its first act is rebuilding this
+    // wavefront's weight tile(s) of chunk j + 1 into `nxt` from records
+    // fetched during iteration j - 1; then it fetches the records of chunk
+    // j + 2 and issues the direct-to-LDS activation loads of chunk j + 1, so
+    // both kinds of load have a whole iteration of MFMAs to arrive.  (The LDS
+    // writes come before the direct loads because the compiler makes any LDS
+    // store wait for direct-to-LDS loads still in flight.)
+    const std::integral_constant<bool, false> stage0;
+    const std::integral_constant<bool, true> stage1;
+    if (nchunks > 0) {
+        fetch_w(0);
+        rebuild_w(stage0);
+        issue_act(0, stage0);
+        if (nchunks > 1) fetch_w(1);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int64_t j = 0; j < nfull; ++j) {
-        const int buf = (int)(j & 1);
-        // buffer buf ^ 1 was last read before the previous barrier
-        if (j + 1 < nfull) issue_direct(j + 1, buf ^ 1);
-        const uint8_t *base = lds + buf * L::kStage;
-        compute_step(base, 0);
-        compute_step(base, 1);
-        if (j + 1 < nfull) store_sc(buf ^ 1);
-        __builtin_amdgcn_s_waitcnt(0);   // direct loads of the next chunk have landed
-        __syncthreads();
+    W4A8_LDS_BARRIER();
+    auto iteration = [&](int64_t j, auto cur, auto nxt) {
+        if (j + 1 < nchunks) rebuild_w(nxt);
+        if (j + 2 < nchunks) fetch_w(j + 2);
+        if (j + 1 < nchunks) issue_act(j + 1, nxt);
+        mma_step(cur, 0);
+        if ((j + 1) * kChunkK <= k) mma_step(cur, 1);
+        W4A8_LDS_BARRIER();
+    };
+    for (int64_t j = 0; j < nchunks; j += 2) {
+        iteration(j, stage0, stage1);
+        if (j + 1 < nchunks) iteration(j + 1, stage1, stage0);
     }
-    if (nfull * kChunkK < k) {
-        // trailing 64-wide chunk (k % 128 == 64), staged through registers
-        const std::integral_constant<bool, false> half_chunk;
-        load_global(nfull, half_chunk);
-        store_lds(0);
-        __syncthreads();
-        compute_step(lds, 0);
-    }
+#undef W4A8_LDS_BARRIER
 
+    // Epilogue straight from the accumulator layout: lane (c, kq) holds output
+    // row c of the row tile and channels 4 kq .. 4 kq + 3 of the channel tile.
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
-        const int64_t nn = n0 + wn * WN + tn * 16 + 4 * kq;
+        const int64_t nn = n0 + (wn * TN + tn) * 16 + 4 * kq;
         if (nn >= n) continue;
         const f32x4 sc = *(const f32x4 *)(ch_scale + nn);
 #pragma unroll
@@ -642,7 +628,7 @@ hipError_t launch_w4a8_gemm(const int8_t *a_q, const float *a_scale, const uint8
         launch_tiled<128, 128, 2, 2>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out,
                                out_dtype, stream);
     } else {
-        launch_tiled<256, 256, 2, 4>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out,
+        launch_tiled<256, 256, 4, 4>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out,
                                out_dtype, stream);
     }
     return hipGetLastError();
