@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-quantizer", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 256 MiB device-to-device copy (reference for the "
+                        "FETCH_SIZE / WRITE_SIZE counters) and exit")
     return p.parse_args()
 
 
@@ -125,6 +128,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        x = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": 4 * x.numel(),
+                          "bytes_written_per_launch": 4 * x.numel(), "launches": 5}))
+        return
     a_bits, w_bits, spec = inputs.workload_inputs(args.workload, seed=0)
     m, n, k = spec["m"], spec["n"], spec["k"]
     out_dtype = torch.bfloat16 if spec["out"] == "bf16" else torch.float32

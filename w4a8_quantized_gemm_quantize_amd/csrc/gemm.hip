@@ -550,17 +550,74 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
     }
 #undef W4A8_LDS_BARRIER
 
-    // Epilogue straight from the accumulator layout: lane (c, kq) holds output
-    // row c of the row tile and channels 4 kq .. 4 kq + 3 of the channel tile.
+    // Epilogue through LDS (free after the last barrier): each wavefront writes
+    // its WM x WN tile of final values (bf16, fp32 or int32) to its own slice of
+    // the stage arrays, then stores whole 128-byte row segments, so each output
+    // cache line is written in full (straight from the accumulator layout a lane
+    // holds only 4 consecutive columns of a row).  16-byte segments are
+    // XOR-swizzled by row % 8 for conflict-free reads.  Four-byte outputs go in
+    // two passes of half the rows.
+    {
+        constexpr int PER_ARRAY = WAVES / 4;
+        static_assert(WAVES % 4 == 0, "four stage arrays share the epilogue");
+        const int esize = (out_dtype == 1) ? 2 : 4;
+        const int rows_pass = (esize == 2) ? WM : WM / 2;
+        const int row_bytes = WN * esize;
+        const int segs = row_bytes / 16;                 // 16-byte segments per row
+        static_assert(WM * WN * 2 <= (L::kW < L::kAct ? L::kW : L::kAct) / PER_ARRAY,
+                      "epilogue tile fits the stage arrays");
+        const int which = wave / PER_ARRAY;
+        uint8_t *ebuf = (which == 0 ? act0 : which == 1 ? act1 : which == 2 ? wl0 : wl1) +
+                        (wave % PER_ARRAY) * (WM * WN * 2);
+        auto seg_off = [&](int r, int seg) { return r * row_bytes + ((seg ^ (r & 7)) << 4); };
+        for (int pass = 0; pass < WM / rows_pass; ++pass) {
+            // accumulators -> LDS (lane (c, kq): row tm * 16 + c, 4 columns)
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-        const int64_t nn = n0 + (wn * TN + tn) * 16 + 4 * kq;
-        if (nn >= n) continue;
-        const f32x4 sc = *(const f32x4 *)(ch_scale + nn);
+            for (int tm = 0; tm < TM; ++tm) {
+                const int r = tm * 16 + c - pass * rows_pass;
+                if (r < 0 || r >= rows_pass) continue;
+                const int64_t row = m0 + wm * WM + tm * 16 + c;
+                const float sa = a_scale[row < m ? row : m - 1];
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-            const int64_t row = m0 + wm * WM + tm * 16 + c;
-            if (row < m) store4(out, out_dtype, row, n, nn, acc[tn][tm], a_scale[row], sc);
+                for (int tn = 0; tn < TN; ++tn) {
+                    const int col = tn * 16 + 4 * kq;             // within the wavefront tile
+                    const int64_t nn = n0 + wn * WN + col;
+                    const int byte = col * esize;
+                    uint8_t *dst = ebuf + seg_off(r, byte >> 4) + (byte & 15);
+                    const v4i a4 = acc[tn][tm];
+                    if (out_dtype == 2) {
+                        *(v4i *)dst = a4;
+                    } else {
+                        const f32x4 sc = *(const f32x4 *)(ch_scale + (nn < n ? nn : n - 4));
+                        float y[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            y[i] = (float)a4[i] * sa;
+                            y[i] = y[i] * sc[i];
+                        }
+                        if (out_dtype == 1)
+                            *(u32x2 *)dst = u32x2{f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16),
+                                                  f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16)};
+                        else
+                            *(f32x4 *)dst = f32x4{y[0], y[1], y[2], y[3]};
+                    }
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wavefront's LDS writes done
+            asm volatile("" ::: "memory");
+            // LDS -> global: 16 bytes per lane, whole rows of the wavefront tile
+            const int lanes_per_row = segs;               // 8 (bf16) or 16 (4-byte)
+            const int rows_per_iter = 64 / lanes_per_row;
+            for (int r0 = 0; r0 < rows_pass; r0 += rows_per_iter) {
+                const int r = r0 + lane / lanes_per_row;
+                const int seg = lane % lanes_per_row;
+                const int64_t row = m0 + wm * WM + pass * rows_pass + r;
+                const int64_t nn = n0 + wn * WN + (seg * 16) / esize;
+                const u32x4 v = *(const u32x4 *)(ebuf + seg_off(r, seg));
+                if (row < m && nn < n)
+                    *(u32x4 *)((uint8_t *)out + (row * n + nn) * esize) = v;
+            }
+            asm volatile("" ::: "memory");
         }
     }
 }
