@@ -57,10 +57,10 @@ def parse():
 
 def gemm_algorithmic_bytes(m, n, k, out_bytes, fused):
     """Bytes the W4A8 GEMM must move: int4 weights, uint8 group scales, fp32 channel
-    scales and the output, each once; plus the activations: bf16 in and the int8
-    codes + fp32 row scales out when quantization is fused into the kernel, else
-    the int8 codes + row scales in."""
-    act = (2 * m * k + m * k + 4 * m) if fused else (m * k + 4 * m)
+    scales and the output, each once; plus the activations once: bf16 when
+    quantization is fused into the kernel (the int8 codes it also leaves in the
+    workspace are not counted), else the int8 codes + fp32 row scales."""
+    act = 2 * m * k if fused else (m * k + 4 * m)
     return n * k // 2 + n * (k // 64) + 4 * n + act + m * n * out_bytes
 
 
