@@ -21,6 +21,8 @@ _SRC = os.path.join(_HERE, "oracle_w4a8.c")
 _LIB = os.path.join(_HERE, "liboracle_w4a8.so")
 
 K_MAX = 150976
+# K bound when int8 weight operands reach 127 (LQQ and W8A8 weights).
+K_MAX_127 = 133120
 
 _lib = None
 
@@ -57,6 +59,13 @@ def _load():
         "oracle_group_sums": [P, P, I64, I64, I64, I32, P],
         "oracle_w4a8_gemm": [P, P, P, P, P, I64, I64, I64, I32, P, P],
         "oracle_w4a8_gemm_bf16act": [P, P, P, P, I64, I64, I64, I32, P, P, P, P],
+        "oracle_quantize_w4_lqq": [P, I64, I64, I32, P, P, P, P],
+        "oracle_dequantize_w4_lqq": [P, P, P, P, I64, I64, I32, P],
+        "oracle_w4a8_gemm_lqq": [P, P, P, P, P, P, I64, I64, I64, I32, P, P],
+        "oracle_w4a8_gemm_blockact": [P, P, P, P, P, I64, I64, I64, I32, I32, P, P],
+        "oracle_quantize_w8_channel": [P, I64, I64, P, P],
+        "oracle_w8a8_gemm": [P, P, P, P, I64, I64, I64, P, P],
+        "oracle_dequant_add_requant": [P, P, P, P, I64, I64, I32, P, P, P],
         "oracle_num_threads": [],
     }
     for name, args in sigs.items():
@@ -199,3 +208,121 @@ def w4a8_gemm_bf16act(a_bf16, q, s_g, s_ch, group: int = 64, want_y: bool = True
                                             group, _ptr(a_q), _ptr(a_s), _ptr(acc), _ptr(y)),
            "w4a8_gemm_bf16act")
     return a_q, a_s, acc, y
+
+
+# ------------------------------------------------------------- extensions --
+
+def quantize_w4_lqq(w_bf16: np.ndarray, group: int = 64):
+    """LQQ weights: bf16 bits [n, k] -> (q_u4 uint8 [n,k] in [0,15], s_u8 uint8
+    [n,k/group], w_min int8 [n,k/group], s_ch f32 [n])."""
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    n, k = w.shape
+    if group <= 0 or k % group:
+        raise ValueError("k must be a multiple of group")
+    q = np.empty((n, k), np.uint8)
+    s_u8 = np.empty((n, k // group), np.uint8)
+    w_min = np.empty((n, k // group), np.int8)
+    s_ch = np.empty((n,), np.float32)
+    _check(_load().oracle_quantize_w4_lqq(_ptr(w), n, k, group, _ptr(q), _ptr(s_u8),
+                                          _ptr(w_min), _ptr(s_ch)),
+           "quantize_w4_lqq")
+    return q, s_u8, w_min, s_ch
+
+
+def dequantize_w4_lqq(q_u4, s_u8, w_min, s_ch, group: int = 64):
+    q_u4 = np.ascontiguousarray(q_u4, dtype=np.uint8)
+    s_u8 = np.ascontiguousarray(s_u8, dtype=np.uint8)
+    w_min = np.ascontiguousarray(w_min, dtype=np.int8)
+    s_ch = np.ascontiguousarray(s_ch, dtype=np.float32)
+    n, k = q_u4.shape
+    out = np.empty((n, k), np.float64)
+    _check(_load().oracle_dequantize_w4_lqq(_ptr(q_u4), _ptr(s_u8), _ptr(w_min), _ptr(s_ch),
+                                            n, k, group, _ptr(out)),
+           "dequantize_w4_lqq")
+    return out
+
+
+def w4a8_gemm_lqq(a_q, a_scale, q_u4, s_u8, w_min, s_ch, group: int = 64, want_y=True):
+    """-> (acc int32 [m,n], y f64 [m,n] or None) on LQQ weights."""
+    a_q = np.ascontiguousarray(a_q, dtype=np.int8)
+    a_scale = np.ascontiguousarray(a_scale, dtype=np.float32).reshape(-1)
+    q_u4 = np.ascontiguousarray(q_u4, dtype=np.uint8)
+    s_u8 = np.ascontiguousarray(s_u8, dtype=np.uint8)
+    w_min = np.ascontiguousarray(w_min, dtype=np.int8)
+    s_ch = np.ascontiguousarray(s_ch, dtype=np.float32)
+    m, k = a_q.shape
+    n = q_u4.shape[0]
+    acc = np.empty((m, n), np.int32)
+    y = np.empty((m, n), np.float64) if want_y else None
+    _check(_load().oracle_w4a8_gemm_lqq(_ptr(a_q), _ptr(a_scale), _ptr(q_u4), _ptr(s_u8),
+                                        _ptr(w_min), _ptr(s_ch), m, n, k, group, _ptr(acc),
+                                        _ptr(y)),
+           "w4a8_gemm_lqq")
+    return acc, y
+
+
+def w4a8_gemm_blockact(a_q, a_scale, q, s_g, s_ch, block: int, group: int = 64):
+    """Per-block activation scales a_scale [m, k/block] -> (y f64 [m,n], bound f64 [m,n])."""
+    a_q = np.ascontiguousarray(a_q, dtype=np.int8)
+    a_scale = np.ascontiguousarray(a_scale, dtype=np.float32)
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s_g = np.ascontiguousarray(s_g, dtype=np.uint8)
+    s_ch = np.ascontiguousarray(s_ch, dtype=np.float32)
+    m, k = a_q.shape
+    n = q.shape[0]
+    if a_scale.shape != (m, k // block):
+        raise ValueError("a_scale must be [m, k/block]")
+    y = np.empty((m, n), np.float64)
+    bound = np.empty((m, n), np.float64)
+    _check(_load().oracle_w4a8_gemm_blockact(_ptr(a_q), _ptr(a_scale), _ptr(q), _ptr(s_g),
+                                             _ptr(s_ch), m, n, k, group, block, _ptr(y),
+                                             _ptr(bound)),
+           "w4a8_gemm_blockact")
+    return y, bound
+
+
+def quantize_w8_channel(w_bf16: np.ndarray):
+    """bf16 bits [n, k] -> (q8 int8 [n,k] in [-127,127], s_ch f32 [n])."""
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    n, k = w.shape
+    q8 = np.empty((n, k), np.int8)
+    s_ch = np.empty((n,), np.float32)
+    _check(_load().oracle_quantize_w8_channel(_ptr(w), n, k, _ptr(q8), _ptr(s_ch)),
+           "quantize_w8_channel")
+    return q8, s_ch
+
+
+def w8a8_gemm(a_q, a_scale, q8, s_ch, want_y=True):
+    a_q = np.ascontiguousarray(a_q, dtype=np.int8)
+    a_scale = np.ascontiguousarray(a_scale, dtype=np.float32).reshape(-1)
+    q8 = np.ascontiguousarray(q8, dtype=np.int8)
+    s_ch = np.ascontiguousarray(s_ch, dtype=np.float32)
+    m, k = a_q.shape
+    n = q8.shape[0]
+    acc = np.empty((m, n), np.int32)
+    y = np.empty((m, n), np.float64) if want_y else None
+    _check(_load().oracle_w8a8_gemm(_ptr(a_q), _ptr(a_scale), _ptr(q8), _ptr(s_ch), m, n, k,
+                                    _ptr(acc), _ptr(y)),
+           "w8a8_gemm")
+    return acc, y
+
+
+def dequant_add_requant(q_in, s_in, x, block: int, want_sum: bool = True):
+    """EQuARX receive step.  x is float32 [rows, cols] or bf16 bits (uint16).
+    -> (q_out int8, s_out f32 [rows, cols/block], sum f32 or None)."""
+    q_in = np.ascontiguousarray(q_in, dtype=np.int8)
+    s_in = np.ascontiguousarray(s_in, dtype=np.float32)
+    rows, cols = q_in.shape
+    if x.dtype == np.float32:
+        xf, xb = np.ascontiguousarray(x), None
+    elif x.dtype == np.uint16:
+        xf, xb = None, np.ascontiguousarray(x)
+    else:
+        raise TypeError("x must be float32 or bf16 bits (uint16)")
+    q = np.empty((rows, cols), np.int8)
+    s = np.empty((rows, cols // block), np.float32)
+    v = np.empty((rows, cols), np.float32) if want_sum else None
+    _check(_load().oracle_dequant_add_requant(_ptr(q_in), _ptr(s_in), _ptr(xf), _ptr(xb), rows,
+                                              cols, block, _ptr(v), _ptr(q), _ptr(s)),
+           "dequant_add_requant")
+    return q, s, v

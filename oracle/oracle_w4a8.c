@@ -45,6 +45,26 @@
  *   R5  GEMM: per-token activation scales; acc = sum_g s_g * P_g in int32
  *       where P_g is the int32 dot product over group g; the real output is
  *       acc * s_a[m] * s_ch[n], computed here in binary64.
+ *
+ * Readings for the extensions further down (same pages):
+ *   R6  LQQ weights (LiquidGEMM's own asymmetric format): level 1 per channel
+ *       with protective range 119, Q = clamp(rne(w * fl(119/c)), -119, 119),
+ *       s_ch = c/119.  Level 2 per group of 64: min and max of Q; integer
+ *       scale s_u8 = max(1, nearest integer to (max - min)/15) -- the page's
+ *       bound of 16 on s_u8 holds for rounding to nearest (a tie cannot occur:
+ *       15 is odd); code q_u4 = rne((Q - min)/s_u8) clamped to [0, 15]; the
+ *       offset stored with the group is min.  The rebuilt int8 operand is
+ *       q_u4 * s_u8 + min, in [-119, 127].
+ *   R7  Per-block activation scales inside the GEMM (block 32 or a multiple
+ *       of 64): the int32 partial of each activation block is exact; the
+ *       output is s_ch[n] * sum_b s_a[m,b] * partial_b, here in binary64, with
+ *       the bound sum_b |s_a[m,b] * partial_b| * s_ch[n] that fixes the
+ *       tolerance of a binary32 fold.
+ *   R8  W8A8 comparison path: symmetric int8 weights per channel (range
+ *       127), per-token int8 activations, exact int32 accumulation.
+ *   R9  EQuARX local reduction step: a received int8 block is dequantized to
+ *       binary32 (q * s), added in binary32 to the local partial sum (binary32,
+ *       or bf16 widened exactly), and the sum is requantized with R1-R3.
  */
 #include <math.h>
 #include <stdint.h>
@@ -372,6 +392,273 @@ int oracle_w4a8_gemm_bf16act(const uint16_t *a, const int8_t *q, const uint8_t *
     if (rc != ORACLE_OK)
         return rc;
     return oracle_w4a8_gemm(a_q_out, a_s_out, q, s_g, s_ch, m, n, k, group, acc, y);
+}
+
+/* ------------------------------------------- extension: LQQ weights -- */
+
+/* Largest K with |acc| <= K * 127 * 127 in int32, rounded down to a multiple
+ * of 64 (LQQ operands reach 127; so do W8A8 weights). */
+#define ORACLE_K_MAX_127 133120
+
+/* Per-channel symmetric int8 level with protective range `range`:
+ * c = max |w|, s_ch = c / range, code = clamp(rne(w * fl(range / c))). */
+static void channel_int8(const uint16_t *w, int64_t n, int64_t k, int range, int8_t *w8,
+                         float *s_ch)
+{
+    const float fr = (float)range;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        const uint16_t *wr = w + r * k;
+        float c = 0.0f;
+        for (int64_t i = 0; i < k; ++i) {
+            float a = fabsf(bf16_bits_to_float(wr[i]));
+            if (a > c)
+                c = a;
+        }
+        s_ch[r] = c / fr;
+        float inv = (c > 0.0f) ? (fr / c) : 0.0f;
+        for (int64_t i = 0; i < k; ++i)
+            w8[r * k + i] = (int8_t)saturating_round_half_even(bf16_bits_to_float(wr[i]) * inv,
+                                                               range);
+    }
+}
+
+/*
+ * LQQ ("LiquidGEMM" verdict page, pith_extraction.key_machinery: the int8
+ * weights are shifted by the group minimum into the unsigned domain, coded on
+ * 4 bits with an integer scale, and rebuilt as (q_u4 * s_u8 + a) XOR 0x80 with
+ * a = 128 + min; referee_report.major_comments[2]: protective range 119 and
+ * s_u8 <= 16).  Reading R6.  Outputs in plain row-major order:
+ * q_u4 [n,k] in [0,15], s_u8 [n,k/group] in [1,16], w_min [n,k/group] in
+ * [-119,119], s_ch [n].
+ */
+int oracle_quantize_w4_lqq(const uint16_t *w, int64_t n, int64_t k, int32_t group,
+                           uint8_t *q_u4, uint8_t *s_u8, int8_t *w_min, float *s_ch)
+{
+    if (n < 0 || k < 0 || group <= 0 || (k % group) != 0)
+        return ORACLE_BAD_ARGS;
+    if (n == 0)
+        return ORACLE_OK;
+    if (!w || !s_ch)
+        return ORACLE_BAD_ARGS;
+    if (k == 0) {
+        for (int64_t r = 0; r < n; ++r)
+            s_ch[r] = 0.0f;
+        return ORACLE_OK;
+    }
+    if (!q_u4 || !s_u8 || !w_min)
+        return ORACLE_BAD_ARGS;
+    int8_t *w8 = (int8_t *)malloc((size_t)(n * k));
+    if (!w8)
+        return ORACLE_BAD_ARGS;
+    channel_int8(w, n, k, 119, w8, s_ch);
+    const int64_t ng = k / group;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t g = 0; g < ng; ++g) {
+            const int8_t *src = w8 + r * k + g * group;
+            int lo = src[0], hi = src[0];
+            for (int32_t i = 1; i < group; ++i) {
+                if (src[i] < lo)
+                    lo = src[i];
+                if (src[i] > hi)
+                    hi = src[i];
+            }
+            /* nearest integer to (hi - lo) / 15; 15 is odd, so never a tie */
+            int span = hi - lo;
+            int s = span / 15 + ((span % 15) * 2 > 15 ? 1 : 0);
+            if (s < 1)
+                s = 1;
+            s_u8[r * ng + g] = (uint8_t)s;
+            w_min[r * ng + g] = (int8_t)lo;
+            for (int32_t i = 0; i < group; ++i) {
+                int v = div_round_half_even(src[i] - lo, s);
+                if (v > 15)
+                    v = 15;
+                q_u4[r * k + g * group + i] = (uint8_t)v;
+            }
+        }
+    }
+    free(w8);
+    return ORACLE_OK;
+}
+
+/* Effective LQQ weight s_ch[n] * (q_u4 * s_u8 + min) in binary64. */
+int oracle_dequantize_w4_lqq(const uint8_t *q_u4, const uint8_t *s_u8, const int8_t *w_min,
+                             const float *s_ch, int64_t n, int64_t k, int32_t group,
+                             double *w_hat)
+{
+    if (n < 0 || k < 0 || group <= 0 || (k % group) != 0)
+        return ORACLE_BAD_ARGS;
+    const int64_t ng = k / group;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t i = 0; i < k; ++i) {
+            int g = (int)(i / group);
+            int op = (int)q_u4[r * k + i] * (int)s_u8[r * ng + g] + (int)w_min[r * ng + g];
+            w_hat[r * k + i] = (double)s_ch[r] * (double)op;
+        }
+    return ORACLE_OK;
+}
+
+/*
+ * W4A8 GEMM on LQQ weights: acc[m,n] = sum_k a_q[m,k] * (q_u4 * s_u8 + min)
+ * in int32 (exact: |acc| <= K * 127 * 127), y = acc * s_a[m] * s_ch[n] in
+ * binary64 (may be NULL).
+ */
+int oracle_w4a8_gemm_lqq(const int8_t *a_q, const float *a_scale, const uint8_t *q_u4,
+                         const uint8_t *s_u8, const int8_t *w_min, const float *s_ch,
+                         int64_t m, int64_t n, int64_t k, int32_t group, int32_t *acc,
+                         double *y)
+{
+    if (m < 0 || n < 0 || k < 0 || group <= 0 || (k % group) != 0 || k > ORACLE_K_MAX_127)
+        return ORACLE_BAD_ARGS;
+    const int64_t ng = k / group;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i) {
+        for (int64_t j = 0; j < n; ++j) {
+            int32_t total = 0;
+            for (int64_t t = 0; t < k; ++t) {
+                int64_t g = t / group;
+                int32_t op = (int32_t)q_u4[j * k + t] * (int32_t)s_u8[j * ng + g] +
+                             (int32_t)w_min[j * ng + g];
+                total += (int32_t)a_q[i * k + t] * op;
+            }
+            if (acc)
+                acc[i * n + j] = total;
+            if (y)
+                y[i * n + j] = (double)total * (double)a_scale[i] * (double)s_ch[j];
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------- extension: per-block activation scales in the GEMM -- */
+
+/*
+ * Reading R7.  a_scale is [m, k/block] (the block quantizer's scales);
+ * block is 32 or a multiple of the weight group 64, and divides k.
+ *   partial_b[m,n] = sum_{k in block b} a_q[m,k] * q[n,k] * s_g[n, k/group]  (int32)
+ *   y[m,n]     = s_ch[n] * sum_b s_a[m,b] * partial_b                       (binary64)
+ *   bound[m,n] = s_ch[n] * sum_b |s_a[m,b] * partial_b|                     (binary64)
+ * bound (may be NULL) scales the error of any binary32 evaluation of the sum.
+ */
+int oracle_w4a8_gemm_blockact(const int8_t *a_q, const float *a_scale, const int8_t *q,
+                              const uint8_t *s_g, const float *s_ch, int64_t m, int64_t n,
+                              int64_t k, int32_t group, int32_t block, double *y,
+                              double *bound)
+{
+    if (m < 0 || n < 0 || k < 0 || group <= 0 || (k % group) != 0 || k > ORACLE_K_MAX ||
+        block <= 0 || (k % block) != 0 || !(group % block == 0 || block % group == 0))
+        return ORACLE_BAD_ARGS;
+    const int64_t ng = k / group, nb = k / block;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i) {
+        for (int64_t j = 0; j < n; ++j) {
+            double sum = 0.0, mag = 0.0;
+            for (int64_t b = 0; b < nb; ++b) {
+                int32_t part = 0;
+                for (int64_t t = b * block; t < (b + 1) * block; ++t)
+                    part += (int32_t)a_q[i * k + t] * (int32_t)q[j * k + t] *
+                            (int32_t)s_g[j * ng + t / group];
+                double term = (double)a_scale[i * nb + b] * (double)part;
+                sum += term;
+                mag += fabs(term);
+            }
+            y[i * n + j] = sum * (double)s_ch[j];
+            if (bound)
+                bound[i * n + j] = mag * (double)s_ch[j];
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------- extension: W8A8 comparison path -- */
+
+/* Reading R8: per-channel symmetric int8 weights, c = max |w|, s_ch = c/127. */
+int oracle_quantize_w8_channel(const uint16_t *w, int64_t n, int64_t k, int8_t *q8,
+                               float *s_ch)
+{
+    if (n < 0 || k < 0)
+        return ORACLE_BAD_ARGS;
+    if (n == 0)
+        return ORACLE_OK;
+    if (!w || !s_ch || (k > 0 && !q8))
+        return ORACLE_BAD_ARGS;
+    channel_int8(w, n, k, 127, q8, s_ch);
+    return ORACLE_OK;
+}
+
+/* acc[m,n] = sum_k a_q[m,k] * q8[n,k] (int32), y = acc * s_a[m] * s_ch[n] (binary64). */
+int oracle_w8a8_gemm(const int8_t *a_q, const float *a_scale, const int8_t *q8,
+                     const float *s_ch, int64_t m, int64_t n, int64_t k, int32_t *acc,
+                     double *y)
+{
+    if (m < 0 || n < 0 || k < 0 || k > ORACLE_K_MAX_127)
+        return ORACLE_BAD_ARGS;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            int32_t total = 0;
+            for (int64_t t = 0; t < k; ++t)
+                total += (int32_t)a_q[i * k + t] * (int32_t)q8[j * k + t];
+            if (acc)
+                acc[i * n + j] = total;
+            if (y)
+                y[i * n + j] = (double)total * (double)a_scale[i] * (double)s_ch[j];
+        }
+    return ORACLE_OK;
+}
+
+/* ------------------------- extension: EQuARX local reduction step (R9) -- */
+
+/*
+ * One receive step of a block-quantized reduce-scatter ("EQuARX" verdict page,
+ * pith_extraction.key_machinery: received blocks are dequantized to FP32 before
+ * the partial-sum addition; the sum is block-quantized again for the next hop).
+ *   d = fl(q_in * s_in);  v = fl(x + d)  with x binary32 (x_f32) or bf16 (x_bf16)
+ *   (q_out, s_out) = block quantization of v (R1-R3 on binary32 input)
+ * sum_out (may be NULL) receives v.  Exactly one of x_f32 / x_bf16 is given.
+ */
+int oracle_dequant_add_requant(const int8_t *q_in, const float *s_in, const float *x_f32,
+                               const uint16_t *x_bf16, int64_t rows, int64_t cols,
+                               int32_t block, float *sum_out, int8_t *q_out, float *s_out)
+{
+    if (rows < 0 || cols < 0 || block <= 0 || (cols % block) != 0 ||
+        (x_f32 == NULL) == (x_bf16 == NULL))
+        return ORACLE_BAD_ARGS;
+    if (rows == 0 || cols == 0)
+        return ORACLE_OK;
+    if (!q_in || !s_in || !q_out || !s_out)
+        return ORACLE_BAD_ARGS;
+    const int64_t nblk = cols / block;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        float *v = (float *)malloc(sizeof(float) * (size_t)block);
+        for (int64_t b = 0; b < nblk; ++b) {
+            const int64_t base = r * cols + b * block;
+            const float sb = s_in[r * nblk + b];
+            float amax = 0.0f;
+            for (int32_t i = 0; i < block; ++i) {
+                float d = (float)q_in[base + i] * sb;
+                float x = x_f32 ? x_f32[base + i] : bf16_bits_to_float(x_bf16[base + i]);
+                v[i] = x + d;
+                float a = fabsf(v[i]);
+                if (a > amax)
+                    amax = a;
+            }
+            float s = amax / 127.0f;
+            float inv = (amax > 0.0f) ? (127.0f / amax) : 0.0f;
+            s_out[r * nblk + b] = s;
+            for (int32_t i = 0; i < block; ++i) {
+                q_out[base + i] = (int8_t)saturating_round_half_even(v[i] * inv, 127);
+                if (sum_out)
+                    sum_out[base + i] = v[i];
+            }
+        }
+        free(v);
+    }
+    return ORACLE_OK;
 }
 
 /* Number of threads the OpenMP regions above use. */
