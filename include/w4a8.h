@@ -185,6 +185,94 @@ w4a8_status w4a8_gemm_bf16act(const uint16_t *a, const uint8_t *w_packed,
                               w4a8_dtype out_dtype, void *workspace, size_t ws_bytes,
                               hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * LQQ weights: LiquidGEMM's own asymmetric 4-bit format ("LiquidGEMM" verdict
+ * page, pith_extraction.key_machinery: INT8 weights shifted by the group
+ * minimum into the unsigned domain, 4-bit codes with an integer scale, and the
+ * rebuild (q_u4 * s_u8 + a) XOR 0x80 with a = 128 + min;
+ * referee_report.major_comments[2] (paper section 4, Eq. 7): protective range
+ * 119 and s_u8 <= 16).
+ * ------------------------------------------------------------------------ */
+
+/* Largest K for which |acc| <= K * 127 * 127 fits in int32 (multiple of 64):
+ * the bound when weight operands reach 127 (LQQ and int8 weights). */
+#define W4A8_LQQ_K_MAX 133120
+
+/*
+ * LQQ quantization and packing.
+ *   w         [n, k] bf16 (input)
+ *   w_packed  n * k / 2 bytes, layout V1 (nibble = q_u4) (output)
+ *   grp_param n * k / 64 uint16, kernel order like grp_scale:
+ *             s_u8 | (128 + min) << 8 (output)
+ *   ch_scale  [n] binary32 (output)
+ * Per channel: c = max |w|, ch_scale = c / 119,
+ *   Q = clamp(round_half_even(w * (119 / c)), -119, 119)  (0 when c == 0).
+ * Per group of 64: min, max of Q; s_u8 = max(1, nearest integer to
+ *   (max - min) / 15) in [1, 16]; q_u4 = min(15, round_half_even((Q - min) / s_u8)).
+ * Effective weight: ch_scale[n] * (q_u4 * s_u8 + min); the int8 operand
+ * q_u4 * s_u8 + min lies in [-119, 127].  Shape rules as for pack_w4_grouped.
+ */
+w4a8_status pack_w4_lqq(const uint16_t *w, int64_t n, int64_t k, int32_t group,
+                        uint8_t *w_packed, uint16_t *grp_param, float *ch_scale,
+                        hipStream_t stream);
+
+/* Inverse (test hook): q_u4 [n, k] uint8 in [0, 15], s_u8 [n, k/64] uint8,
+ * w_min [n, k/64] int8, all plain row-major. */
+w4a8_status unpack_w4_lqq(const uint8_t *w_packed, const uint16_t *grp_param, int64_t n,
+                          int64_t k, int32_t group, uint8_t *q_u4, uint8_t *s_u8,
+                          int8_t *w_min, hipStream_t stream);
+
+/*
+ * W4A8 GEMM on LQQ weights, per-token activation scales:
+ *   acc[m, n] = sum_k a_q[m, k] * (q_u4[n, k] * s_u8[n, g] + min[n, g])  (int32, exact)
+ *   out as for w4a8_gemm.  Requires k <= W4A8_LQQ_K_MAX and the w4a8_gemm rules.
+ */
+w4a8_status w4a8_gemm_lqq(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
+                          const uint16_t *grp_param, const float *ch_scale, int64_t m,
+                          int64_t n, int64_t k, int32_t group, void *out, w4a8_dtype out_dtype,
+                          hipStream_t stream);
+
+/* Fused per-token quantization + w4a8_gemm_lqq (workspace as for w4a8_gemm_bf16act). */
+w4a8_status w4a8_gemm_lqq_bf16act(const uint16_t *a, const uint8_t *w_packed,
+                                  const uint16_t *grp_param, const float *ch_scale, int64_t m,
+                                  int64_t n, int64_t k, int32_t group, void *out,
+                                  w4a8_dtype out_dtype, void *workspace, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * W8A8 comparison path: per-channel symmetric int8 weights on the same MFMA
+ * core, to test the regime claim of the "LiquidGEMM" verdict page
+ * (pith_extraction.forward_implications: W4A8 wins when memory-bound and
+ * matches W8A8 when compute-bound).
+ * ------------------------------------------------------------------------ */
+
+/*
+ * w [n, k] bf16 -> w_packed n * k bytes (int8, opaque tiled layout),
+ * ch_scale [n] binary32.  Per channel: c = max |w|, ch_scale = c / 127,
+ * q8 = clamp(round_half_even(w * (127 / c)), -127, 127).
+ * Requires n % 16 == 0 and k % 64 == 0.
+ */
+w4a8_status pack_w8_channel(const uint16_t *w, int64_t n, int64_t k, int8_t *w_packed,
+                            float *ch_scale, hipStream_t stream);
+
+/* Inverse (test hook): q8 [n, k] int8, row-major. */
+w4a8_status unpack_w8_channel(const int8_t *w_packed, int64_t n, int64_t k, int8_t *q8,
+                              hipStream_t stream);
+
+/*
+ * acc[m, n] = sum_k a_q[m, k] * q8[n, k] (int32, exact);
+ * out[m, n] = (float(acc) * a_scale[m]) * ch_scale[n], as for w4a8_gemm.
+ * Requires n % 16 == 0, k % 64 == 0, k <= W4A8_LQQ_K_MAX.
+ */
+w4a8_status w8a8_gemm(const int8_t *a_q, const float *a_scale, const int8_t *w_packed,
+                      const float *ch_scale, int64_t m, int64_t n, int64_t k, void *out,
+                      w4a8_dtype out_dtype, hipStream_t stream);
+
+/* Fused per-token quantization + w8a8_gemm (workspace as for w4a8_gemm_bf16act). */
+w4a8_status w8a8_gemm_bf16act(const uint16_t *a, const int8_t *w_packed, const float *ch_scale,
+                              int64_t m, int64_t n, int64_t k, void *out, w4a8_dtype out_dtype,
+                              void *workspace, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,185 @@
+"""GPU parity of the extension paths with the CPU oracle, through the C ABI:
+LQQ (LiquidGEMM's asymmetric 4-bit weights) and the W8A8 comparison path.
+
+Same bar as the main path: codes, scales, group parameters and raw int32
+accumulators bit-exact; binary32 outputs within 1e-5 relative; bf16 outputs
+within one bf16 ulp of the oracle's binary64 value.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from w4a8_quantized_gemm_quantize_amd import inputs
+
+from gpu_util import assert_bf16_within_ulp, assert_f32_close, bits_of, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def w4a8():
+    from w4a8_quantized_gemm_quantize_amd import binding
+    torch.cuda.init()
+    return binding
+
+
+def announce(*what):
+    print("CASE", *what, flush=True)
+
+
+def edge_weights(n, k, seed):
+    """Seeded N(0, 0.02^2) weights plus rows the formats must handle: a zero
+    row, a constant row, a single outlier, a narrow ramp, an all-positive row."""
+    w = (inputs.weights(n, k, seed).astype(np.uint32) << 16).view(np.float32).copy()
+    if n >= 16:
+        w[1] = 0.0
+        w[2] = 0.0125
+        w[3, 5] = 1.0
+        w[4] = np.linspace(-0.01, 0.011, k, dtype=np.float32)
+        w[5] = np.abs(w[5]) + 0.5
+        w[6, 64:128] = 0.0                      # a zero group inside a live row
+    return inputs.f32_to_bf16_bits(w)
+
+
+GEMM_SHAPES = [
+    (16, 256, 256),
+    (1, 16, 64),
+    (5, 48, 192),       # ragged M, trailing half chunk
+    (8, 4096, 4096),    # decode shape
+    (17, 32, 320),
+    (64, 64, 448),
+    (65, 48, 192),      # tiled path, ragged N
+    (200, 272, 384),
+    (129, 144, 4160),
+]
+
+
+# ------------------------------------------------------------------ LQQ --
+
+@pytest.mark.parametrize("n,k", [(256, 256), (48, 192), (16, 64), (4096, 4096), (80, 28672)])
+def test_lqq_pack_roundtrip_matches_oracle(w4a8, n, k):
+    announce("lqq pack", n, k)
+    w = edge_weights(n, k, seed=n + k)
+    wp, gp, cs = w4a8.pack_w4_lqq(to_dev_bf16(w))
+    q, s, mn = w4a8.unpack_w4_lqq(wp, gp, n, k)
+    torch.cuda.synchronize()
+    q_ref, s_ref, mn_ref, cs_ref = oracle.quantize_w4_lqq(w, 64)
+    assert np.array_equal(cs.cpu().numpy().view(np.uint32), cs_ref.view(np.uint32))
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.array_equal(mn.cpu().numpy(), mn_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+def _lqq_pack(w4a8, n, k, seed):
+    w = edge_weights(n, k, seed)
+    return w4a8.pack_w4_lqq(to_dev_bf16(w)), oracle.quantize_w4_lqq(w, 64)
+
+
+@pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
+def test_lqq_gemm_int32_bit_exact(w4a8, m, n, k):
+    announce("lqq gemm i32", m, n, k)
+    dev_w, ref_w = _lqq_pack(w4a8, n, k, seed=m + n)
+    a_q, a_s = oracle.quantize_act_blockwise(inputs.activations(m, k, seed=m, outlier_frac=0.001), k)
+    acc = w4a8.w4a8_gemm_lqq(torch.from_numpy(a_q).cuda(),
+                             torch.from_numpy(a_s.reshape(-1)).cuda(), *dev_w, n,
+                             out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    acc_ref, _ = oracle.w4a8_gemm_lqq(a_q, a_s, *ref_w, 64, want_y=False)
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+
+
+@pytest.mark.parametrize("m,n,k", [(16, 256, 256), (5, 48, 192), (200, 272, 384),
+                                   (8, 4096, 4096)])
+def test_lqq_gemm_float_outputs_and_fused(w4a8, m, n, k):
+    announce("lqq gemm f32/bf16 + fused", m, n, k)
+    dev_w, ref_w = _lqq_pack(w4a8, n, k, seed=3 * m + n)
+    a = inputs.activations(m, k, seed=2 * m, outlier_frac=0.001)
+    a_q, a_s = oracle.quantize_act_blockwise(a, k)
+    aq_d = torch.from_numpy(a_q).cuda()
+    as_d = torch.from_numpy(a_s.reshape(-1)).cuda()
+    y32 = w4a8.w4a8_gemm_lqq(aq_d, as_d, *dev_w, n, out_dtype=torch.float32)
+    y16 = w4a8.w4a8_gemm_lqq(aq_d, as_d, *dev_w, n, out_dtype=torch.bfloat16)
+    ws = torch.empty(w4a8.workspace_bytes(m, k), dtype=torch.uint8, device="cuda")
+    yf = w4a8.w4a8_gemm_lqq_bf16act(to_dev_bf16(a), *dev_w, n, out_dtype=torch.float32,
+                                    workspace=ws)
+    torch.cuda.synchronize()
+    _, y_ref = oracle.w4a8_gemm_lqq(a_q, a_s, *ref_w, 64)
+    assert_f32_close(y32.cpu().numpy(), y_ref)
+    assert_bf16_within_ulp(bits_of(y16), y_ref)
+    ws_q, ws_s = w4a8.workspace_views(ws, m, k)
+    assert np.array_equal(ws_q.cpu().numpy(), a_q)
+    assert np.array_equal(ws_s.cpu().numpy().view(np.uint32), a_s.reshape(-1).view(np.uint32))
+    assert torch.equal(yf.view(torch.int32), y32.view(torch.int32))
+
+
+def test_lqq_extreme_operands(w4a8):
+    # codes at +-127 against operands reaching both ends of [-119, 127]
+    m, n, k = 16, 32, 1024
+    dev_w, ref_w = _lqq_pack(w4a8, n, k, seed=5)
+    a_q = np.where(np.arange(m * k).reshape(m, k) % 3 == 0, 127, -127).astype(np.int8)
+    a_s = np.ones((m, 1), np.float32)
+    acc = w4a8.w4a8_gemm_lqq(torch.from_numpy(a_q).cuda(), torch.from_numpy(a_s.reshape(-1)).cuda(),
+                             *dev_w, n, out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    acc_ref, _ = oracle.w4a8_gemm_lqq(a_q, a_s, *ref_w, 64, want_y=False)
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+
+
+def test_lqq_rejects_k_beyond_bound(w4a8):
+    k = w4a8.LQQ_K_MAX + 64
+    a = torch.zeros((1, k), dtype=torch.int8, device="cuda")
+    with pytest.raises(w4a8.W4A8Error):
+        w4a8.w4a8_gemm_lqq(a, torch.ones(1, device="cuda"),
+                           torch.zeros(16 * k // 2, dtype=torch.uint8, device="cuda"),
+                           torch.zeros(16 * k // 64, dtype=torch.int16, device="cuda"),
+                           torch.ones(16, device="cuda"), 16)
+
+
+# ------------------------------------------------------------------ W8A8 --
+
+@pytest.mark.parametrize("n,k", [(256, 256), (48, 192), (16, 64), (4096, 4096)])
+def test_w8_pack_roundtrip_matches_oracle(w4a8, n, k):
+    announce("w8 pack", n, k)
+    w = edge_weights(n, k, seed=2 * n + k)
+    wp, cs = w4a8.pack_w8_channel(to_dev_bf16(w))
+    q8 = w4a8.unpack_w8_channel(wp, n, k)
+    torch.cuda.synchronize()
+    q_ref, cs_ref = oracle.quantize_w8_channel(w)
+    assert np.array_equal(cs.cpu().numpy().view(np.uint32), cs_ref.view(np.uint32))
+    assert np.array_equal(q8.cpu().numpy(), q_ref)
+
+
+@pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
+def test_w8a8_gemm_int32_bit_exact(w4a8, m, n, k):
+    announce("w8a8 gemm i32", m, n, k)
+    w = edge_weights(n, k, seed=m + 2 * n)
+    wp, cs = w4a8.pack_w8_channel(to_dev_bf16(w))
+    q_ref, cs_ref = oracle.quantize_w8_channel(w)
+    a_q, a_s = oracle.quantize_act_blockwise(inputs.activations(m, k, seed=m + 1), k)
+    acc = w4a8.w8a8_gemm(torch.from_numpy(a_q).cuda(), torch.from_numpy(a_s.reshape(-1)).cuda(),
+                         wp, cs, n, out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    acc_ref, _ = oracle.w8a8_gemm(a_q, a_s, q_ref, cs_ref, want_y=False)
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+
+
+@pytest.mark.parametrize("m,n,k", [(16, 256, 256), (5, 48, 192), (200, 272, 384),
+                                   (8, 4096, 4096)])
+def test_w8a8_float_outputs_and_fused(w4a8, m, n, k):
+    announce("w8a8 f32/bf16 + fused", m, n, k)
+    w = edge_weights(n, k, seed=m + 3 * n)
+    wp, cs = w4a8.pack_w8_channel(to_dev_bf16(w))
+    q_ref, cs_ref = oracle.quantize_w8_channel(w)
+    a = inputs.activations(m, k, seed=m + 2, outlier_frac=0.001)
+    a_q, a_s = oracle.quantize_act_blockwise(a, k)
+    aq_d = torch.from_numpy(a_q).cuda()
+    as_d = torch.from_numpy(a_s.reshape(-1)).cuda()
+    y32 = w4a8.w8a8_gemm(aq_d, as_d, wp, cs, n, out_dtype=torch.float32)
+    y16 = w4a8.w8a8_gemm(aq_d, as_d, wp, cs, n, out_dtype=torch.bfloat16)
+    yf = w4a8.w8a8_gemm_bf16act(to_dev_bf16(a), wp, cs, n, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _, y_ref = oracle.w8a8_gemm(a_q, a_s, q_ref, cs_ref)
+    assert_f32_close(y32.cpu().numpy(), y_ref)
+    assert_bf16_within_ulp(bits_of(y16), y_ref)
+    assert torch.equal(yf.view(torch.int32), y32.view(torch.int32))

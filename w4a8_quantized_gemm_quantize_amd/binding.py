@@ -27,6 +27,7 @@ F32, BF16, I32 = 0, 1, 2
 GROUP = 64
 N_TILE = 16
 K_MAX = 150976
+LQQ_K_MAX = 133120
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -44,6 +45,17 @@ _SIGS = {
     "w4a8_gemm_bf16act_workspace_bytes": ([_I64, _I64], ctypes.c_size_t),
     "w4a8_gemm_bf16act": ([_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, ctypes.c_int, _P,
                            ctypes.c_size_t, _P], ctypes.c_int),
+    "pack_w4_lqq": ([_P, _I64, _I64, _I32, _P, _P, _P, _P], ctypes.c_int),
+    "unpack_w4_lqq": ([_P, _P, _I64, _I64, _I32, _P, _P, _P, _P], ctypes.c_int),
+    "w4a8_gemm_lqq": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, ctypes.c_int, _P],
+                      ctypes.c_int),
+    "w4a8_gemm_lqq_bf16act": ([_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, ctypes.c_int, _P,
+                               ctypes.c_size_t, _P], ctypes.c_int),
+    "pack_w8_channel": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "unpack_w8_channel": ([_P, _I64, _I64, _P, _P], ctypes.c_int),
+    "w8a8_gemm": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P], ctypes.c_int),
+    "w8a8_gemm_bf16act": ([_P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P, ctypes.c_size_t,
+                           _P], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -198,3 +210,110 @@ def workspace_views(workspace, m: int, k: int):
     a_q = workspace[: m * k].view(torch.int8).view(m, k)
     a_s = workspace[off: off + 4 * m].view(torch.float32)
     return a_q, a_s
+
+
+# ------------------------------------------------------------ LQQ weights --
+
+def pack_w4_lqq(w: torch.Tensor, group: int = GROUP, stream=None):
+    """w bf16 [n, k] -> (w_packed uint8 [n*k/2], grp_param int16 [n*k/group] holding
+    uint16 s | (128 + min) << 8, ch_scale f32 [n])."""
+    _dev(w, torch.bfloat16, "w")
+    n, k = w.shape
+    dev = w.device
+    w_packed = torch.empty((n * k // 2,), dtype=torch.uint8, device=dev)
+    grp_param = torch.empty((n * (k // group) if group > 0 else 0,), dtype=torch.int16,
+                            device=dev)
+    ch_scale = torch.empty((n,), dtype=torch.float32, device=dev)
+    _check("pack_w4_lqq",
+           _lib.pack_w4_lqq(_ptr(w), n, k, group, _ptr(w_packed), _ptr(grp_param),
+                            _ptr(ch_scale), _stream(stream)))
+    return w_packed, grp_param, ch_scale
+
+
+def unpack_w4_lqq(w_packed, grp_param, n: int, k: int, group: int = GROUP, stream=None):
+    """Test hook -> (q_u4 uint8 [n, k], s_u8 uint8 [n, k/group], w_min int8 [n, k/group])."""
+    dev = w_packed.device
+    q = torch.empty((n, k), dtype=torch.uint8, device=dev)
+    s_u8 = torch.empty((n, k // group), dtype=torch.uint8, device=dev)
+    w_min = torch.empty((n, k // group), dtype=torch.int8, device=dev)
+    _check("unpack_w4_lqq",
+           _lib.unpack_w4_lqq(_ptr(w_packed), _ptr(grp_param), n, k, group, _ptr(q),
+                              _ptr(s_u8), _ptr(w_min), _stream(stream)))
+    return q, s_u8, w_min
+
+
+def w4a8_gemm_lqq(a_q, a_scale, w_packed, grp_param, ch_scale, n: int,
+                  out_dtype=torch.bfloat16, group: int = GROUP, out=None, stream=None):
+    _dev(a_q, torch.int8, "a_q")
+    m, k = a_q.shape
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a_q.device)
+    _check("w4a8_gemm_lqq",
+           _lib.w4a8_gemm_lqq(_ptr(a_q), _ptr(a_scale), _ptr(w_packed), _ptr(grp_param),
+                              _ptr(ch_scale), m, n, k, group, _ptr(out), _OUT[out.dtype],
+                              _stream(stream)))
+    return out
+
+
+def w4a8_gemm_lqq_bf16act(a, w_packed, grp_param, ch_scale, n: int, out_dtype=torch.bfloat16,
+                          group: int = GROUP, out=None, workspace=None, stream=None):
+    _dev(a, torch.bfloat16, "a")
+    m, k = a.shape
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    if workspace is None:
+        workspace = torch.empty((max(workspace_bytes(m, k), 16),), dtype=torch.uint8,
+                                device=a.device)
+    _check("w4a8_gemm_lqq_bf16act",
+           _lib.w4a8_gemm_lqq_bf16act(_ptr(a), _ptr(w_packed), _ptr(grp_param), _ptr(ch_scale),
+                                      m, n, k, group, _ptr(out), _OUT[out.dtype],
+                                      _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------------ W8A8 --
+
+def pack_w8_channel(w: torch.Tensor, stream=None):
+    """w bf16 [n, k] -> (w_packed int8 [n*k] tiled layout, ch_scale f32 [n])."""
+    _dev(w, torch.bfloat16, "w")
+    n, k = w.shape
+    w_packed = torch.empty((n * k,), dtype=torch.int8, device=w.device)
+    ch_scale = torch.empty((n,), dtype=torch.float32, device=w.device)
+    _check("pack_w8_channel",
+           _lib.pack_w8_channel(_ptr(w), n, k, _ptr(w_packed), _ptr(ch_scale), _stream(stream)))
+    return w_packed, ch_scale
+
+
+def unpack_w8_channel(w_packed, n: int, k: int, stream=None):
+    q8 = torch.empty((n, k), dtype=torch.int8, device=w_packed.device)
+    _check("unpack_w8_channel",
+           _lib.unpack_w8_channel(_ptr(w_packed), n, k, _ptr(q8), _stream(stream)))
+    return q8
+
+
+def w8a8_gemm(a_q, a_scale, w_packed, ch_scale, n: int, out_dtype=torch.bfloat16, out=None,
+              stream=None):
+    _dev(a_q, torch.int8, "a_q")
+    m, k = a_q.shape
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a_q.device)
+    _check("w8a8_gemm",
+           _lib.w8a8_gemm(_ptr(a_q), _ptr(a_scale), _ptr(w_packed), _ptr(ch_scale), m, n, k,
+                          _ptr(out), _OUT[out.dtype], _stream(stream)))
+    return out
+
+
+def w8a8_gemm_bf16act(a, w_packed, ch_scale, n: int, out_dtype=torch.bfloat16, out=None,
+                      workspace=None, stream=None):
+    _dev(a, torch.bfloat16, "a")
+    m, k = a.shape
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    if workspace is None:
+        workspace = torch.empty((max(workspace_bytes(m, k), 16),), dtype=torch.uint8,
+                                device=a.device)
+    _check("w8a8_gemm_bf16act",
+           _lib.w8a8_gemm_bf16act(_ptr(a), _ptr(w_packed), _ptr(ch_scale), m, n, k, _ptr(out),
+                                  _OUT[out.dtype], _ptr(workspace), workspace.numel(),
+                                  _stream(stream)))
+    return out

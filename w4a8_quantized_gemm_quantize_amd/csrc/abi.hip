@@ -41,28 +41,47 @@ w4a8_status check_weight_shape(int64_t n, int64_t k, int32_t group) {
 
 // Shared checks of the GEMM entry points.  `a` is the activation pointer (int8
 // codes or bf16); `a_scale` is only required when need_a_scale is set.
+// grp_scale is the group parameter array of the 4-bit formats; formats without
+// one (int8 weights) pass need_grp = false.  k_max is the format's int32 bound.
 w4a8_status check_gemm_args(const void *a, const float *a_scale, bool need_a_scale,
-                            const uint8_t *w_packed, const uint8_t *grp_scale,
+                            const void *w_packed, const void *grp_scale,
                             const float *ch_scale, int64_t m, int64_t n, int64_t k,
-                            int32_t group, const void *out, w4a8_dtype out_dtype) {
+                            int32_t group, const void *out, w4a8_dtype out_dtype,
+                            int64_t k_max = W4A8_K_MAX, bool need_grp = true) {
     if (m < 0) return W4A8_ERR_SHAPE;
     w4a8_status st = check_weight_shape(n, k, group);
     if (st != W4A8_OK) return st;
-    if (k > W4A8_K_MAX) return W4A8_ERR_UNSUPPORTED;
+    if (k > k_max) return W4A8_ERR_UNSUPPORTED;
     if (out_dtype != W4A8_F32 && out_dtype != W4A8_BF16 && out_dtype != W4A8_I32)
         return W4A8_ERR_UNSUPPORTED;
     if (m == 0 || n == 0) return W4A8_OK;
     const bool has_k = k > 0;
-    if ((has_k && (!a || !w_packed || !grp_scale)) || !ch_scale || !out ||
+    if ((has_k && (!a || !w_packed || (need_grp && !grp_scale))) || !ch_scale || !out ||
         (need_a_scale && !a_scale))
         return W4A8_ERR_NULL;
-    if ((has_k && (!aligned16(a) || !aligned16(w_packed) || !aligned16(grp_scale))) ||
+    if ((has_k && (!aligned16(a) || !aligned16(w_packed) ||
+                   (need_grp && !aligned16(grp_scale)))) ||
         !aligned16(ch_scale) || !aligned16(out) || (need_a_scale && !aligned16(a_scale)))
         return W4A8_ERR_MISALIGNED;
     return W4A8_OK;
 }
 
+// Workspace checks of the fused entry points; on success sets the code and
+// scale pointers inside it.
+w4a8_status split_workspace(void *workspace, size_t ws_bytes, int64_t m, int64_t k,
+                            int8_t **a_q, float **a_s);
+
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+w4a8_status split_workspace(void *workspace, size_t ws_bytes, int64_t m, int64_t k,
+                            int8_t **a_q, float **a_s) {
+    if (!workspace) return W4A8_ERR_NULL;
+    if (!aligned16(workspace)) return W4A8_ERR_MISALIGNED;
+    if (ws_bytes < w4a8_gemm_bf16act_workspace_bytes(m, k)) return W4A8_ERR_SHAPE;
+    *a_q = (int8_t *)workspace;
+    *a_s = (float *)((uint8_t *)workspace + round_up((size_t)m * (size_t)k, 256));
+    return W4A8_OK;
+}
 
 }  // namespace
 
@@ -161,12 +180,126 @@ w4a8_status w4a8_gemm_bf16act(const uint16_t *a, const uint8_t *w_packed,
                                      k, group, out, out_dtype);
     if (st != W4A8_OK) return st;
     if (m == 0 || n == 0) return W4A8_OK;
-    if (!workspace) return W4A8_ERR_NULL;
-    if (!aligned16(workspace)) return W4A8_ERR_MISALIGNED;
-    if (ws_bytes < w4a8_gemm_bf16act_workspace_bytes(m, k)) return W4A8_ERR_SHAPE;
-    int8_t *a_q = (int8_t *)workspace;
-    float *a_s = (float *)((uint8_t *)workspace + round_up((size_t)m * (size_t)k, 256));
+    int8_t *a_q;
+    float *a_s;
+    st = split_workspace(workspace, ws_bytes, m, k, &a_q, &a_s);
+    if (st != W4A8_OK) return st;
     return finish(w4a8::launch_w4a8_gemm_bf16act(a, w_packed, grp_scale, ch_scale, m, n, k, out,
+                                                 (int)out_dtype, a_q, a_s, stream),
+                  stream);
+}
+
+/* ------------------------------------------------ LQQ (asymmetric) weights */
+
+w4a8_status pack_w4_lqq(const uint16_t *w, int64_t n, int64_t k, int32_t group,
+                        uint8_t *w_packed, uint16_t *grp_param, float *ch_scale,
+                        hipStream_t stream) {
+    w4a8_status st = check_weight_shape(n, k, group);
+    if (st != W4A8_OK) return st;
+    if (n == 0) return W4A8_OK;
+    if (!ch_scale || (k > 0 && (!w || !w_packed || !grp_param))) return W4A8_ERR_NULL;
+    if (!aligned16(ch_scale) ||
+        (k > 0 && (!aligned16(w) || !aligned16(w_packed) || !aligned16(grp_param))))
+        return W4A8_ERR_MISALIGNED;
+    return finish(w4a8::launch_pack_w4_lqq(w, n, k, w_packed, grp_param, ch_scale, stream),
+                  stream);
+}
+
+w4a8_status unpack_w4_lqq(const uint8_t *w_packed, const uint16_t *grp_param, int64_t n,
+                          int64_t k, int32_t group, uint8_t *q_u4, uint8_t *s_u8,
+                          int8_t *w_min, hipStream_t stream) {
+    w4a8_status st = check_weight_shape(n, k, group);
+    if (st != W4A8_OK) return st;
+    if (n == 0 || k == 0) return W4A8_OK;
+    if (!w_packed || !grp_param || !q_u4 || !s_u8 || !w_min) return W4A8_ERR_NULL;
+    if (!aligned16(w_packed) || !aligned16(grp_param) || !aligned16(q_u4) || !aligned16(s_u8) ||
+        !aligned16(w_min))
+        return W4A8_ERR_MISALIGNED;
+    return finish(w4a8::launch_unpack_w4_lqq(w_packed, grp_param, n, k, q_u4, s_u8, w_min,
+                                             stream),
+                  stream);
+}
+
+w4a8_status w4a8_gemm_lqq(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
+                          const uint16_t *grp_param, const float *ch_scale, int64_t m,
+                          int64_t n, int64_t k, int32_t group, void *out, w4a8_dtype out_dtype,
+                          hipStream_t stream) {
+    w4a8_status st = check_gemm_args(a_q, a_scale, true, w_packed, grp_param, ch_scale, m, n,
+                                     k, group, out, out_dtype, W4A8_LQQ_K_MAX);
+    if (st != W4A8_OK) return st;
+    if (m == 0 || n == 0) return W4A8_OK;
+    return finish(w4a8::launch_w4a8_gemm_lqq(a_q, a_scale, w_packed, grp_param, ch_scale, m, n,
+                                             k, out, (int)out_dtype, stream),
+                  stream);
+}
+
+w4a8_status w4a8_gemm_lqq_bf16act(const uint16_t *a, const uint8_t *w_packed,
+                                  const uint16_t *grp_param, const float *ch_scale, int64_t m,
+                                  int64_t n, int64_t k, int32_t group, void *out,
+                                  w4a8_dtype out_dtype, void *workspace, size_t ws_bytes,
+                                  hipStream_t stream) {
+    if (k <= 0 || m < 0) return W4A8_ERR_SHAPE;
+    w4a8_status st = check_gemm_args(a, nullptr, false, w_packed, grp_param, ch_scale, m, n, k,
+                                     group, out, out_dtype, W4A8_LQQ_K_MAX);
+    if (st != W4A8_OK) return st;
+    if (m == 0 || n == 0) return W4A8_OK;
+    int8_t *a_q;
+    float *a_s;
+    st = split_workspace(workspace, ws_bytes, m, k, &a_q, &a_s);
+    if (st != W4A8_OK) return st;
+    return finish(w4a8::launch_w4a8_gemm_lqq_bf16act(a, w_packed, grp_param, ch_scale, m, n, k,
+                                                     out, (int)out_dtype, a_q, a_s, stream),
+                  stream);
+}
+
+/* ---------------------------------------------------- W8A8 comparison path */
+
+w4a8_status pack_w8_channel(const uint16_t *w, int64_t n, int64_t k, int8_t *w_packed,
+                            float *ch_scale, hipStream_t stream) {
+    w4a8_status st = check_weight_shape(n, k, W4A8_GROUP);
+    if (st != W4A8_OK) return st;
+    if (n == 0) return W4A8_OK;
+    if (!ch_scale || (k > 0 && (!w || !w_packed))) return W4A8_ERR_NULL;
+    if (!aligned16(ch_scale) || (k > 0 && (!aligned16(w) || !aligned16(w_packed))))
+        return W4A8_ERR_MISALIGNED;
+    return finish(w4a8::launch_pack_w8(w, n, k, w_packed, ch_scale, stream), stream);
+}
+
+w4a8_status unpack_w8_channel(const int8_t *w_packed, int64_t n, int64_t k, int8_t *q8,
+                              hipStream_t stream) {
+    w4a8_status st = check_weight_shape(n, k, W4A8_GROUP);
+    if (st != W4A8_OK) return st;
+    if (n == 0 || k == 0) return W4A8_OK;
+    if (!w_packed || !q8) return W4A8_ERR_NULL;
+    if (!aligned16(w_packed) || !aligned16(q8)) return W4A8_ERR_MISALIGNED;
+    return finish(w4a8::launch_unpack_w8(w_packed, n, k, q8, stream), stream);
+}
+
+w4a8_status w8a8_gemm(const int8_t *a_q, const float *a_scale, const int8_t *w_packed,
+                      const float *ch_scale, int64_t m, int64_t n, int64_t k, void *out,
+                      w4a8_dtype out_dtype, hipStream_t stream) {
+    w4a8_status st = check_gemm_args(a_q, a_scale, true, w_packed, nullptr, ch_scale, m, n, k,
+                                     W4A8_GROUP, out, out_dtype, W4A8_LQQ_K_MAX, false);
+    if (st != W4A8_OK) return st;
+    if (m == 0 || n == 0) return W4A8_OK;
+    return finish(w4a8::launch_w8a8_gemm(a_q, a_scale, w_packed, ch_scale, m, n, k, out,
+                                         (int)out_dtype, stream),
+                  stream);
+}
+
+w4a8_status w8a8_gemm_bf16act(const uint16_t *a, const int8_t *w_packed, const float *ch_scale,
+                              int64_t m, int64_t n, int64_t k, void *out, w4a8_dtype out_dtype,
+                              void *workspace, size_t ws_bytes, hipStream_t stream) {
+    if (k <= 0 || m < 0) return W4A8_ERR_SHAPE;
+    w4a8_status st = check_gemm_args(a, nullptr, false, w_packed, nullptr, ch_scale, m, n, k,
+                                     W4A8_GROUP, out, out_dtype, W4A8_LQQ_K_MAX, false);
+    if (st != W4A8_OK) return st;
+    if (m == 0 || n == 0) return W4A8_OK;
+    int8_t *a_q;
+    float *a_s;
+    st = split_workspace(workspace, ws_bytes, m, k, &a_q, &a_s);
+    if (st != W4A8_OK) return st;
+    return finish(w4a8::launch_w8a8_gemm_bf16act(a, w_packed, ch_scale, m, n, k, out,
                                                  (int)out_dtype, a_q, a_s, stream),
                   stream);
 }

@@ -185,4 +185,85 @@ __device__ __forceinline__ int64_t packed_chunk_offset(int64_t t, int64_t j, int
     return t * (int64_t)kNTile * k / 2 + j * kChunkBytes;
 }
 
+// ------------------------------------------------------- weight formats --
+// The GEMM kernels read three weight formats, all in 16-channel tiles and
+// 128-wide K chunks with the same lane order (lane = c + 16 kq):
+//   kW4Sym  layout V1 above; nibble u = q + 8; parameter per (tile, group,
+//           channel) = uint8 group scale s; operand byte (u s + 128 - 8 s) ^ 0x80.
+//   kW4Lqq  layout V1; nibble u = q_u4 in [0, 15]; parameter = uint16
+//           s | a << 8 with a = 128 + group minimum; operand byte (u s + a) ^ 0x80
+//           = u s + min (LiquidGEMM verdict page, pith_extraction.key_machinery,
+//           in its own asymmetric form).
+//   kW8     int8 weights: chunk j of tile t at t * 16 k + j * 2048; K step h at
+//           + 1024 h, lane record of 16 bytes at + 16 lane (channel c,
+//           k = 128 j + 64 h + 16 kq .. + 15); a trailing 64-wide chunk holds
+//           step 0 only.  No parameter.
+// Parameters are in kernel order [t][g][c] (element t * 16 G + g * 16 + c).
+enum WFmt : int { kW4Sym = 0, kW4Lqq = 1, kW8 = 2 };
+
+template <int WF> struct WRec { u32x4 r; };             // both K steps, 8 B each
+template <> struct WRec<kW8> { u32x4 r0, r1; };         // 16 B per K step
+
+template <int WF>
+__device__ __forceinline__ uint32_t load_wparam(const uint8_t *p, int64_t idx) {
+    if constexpr (WF == kW4Sym) return p[idx];
+    else if constexpr (WF == kW4Lqq) return ((const uint16_t *)p)[idx];
+    else return 0u;
+}
+
+template <int WF>
+__device__ __forceinline__ int64_t wchunk_offset(int64_t t, int64_t j, int64_t k) {
+    if constexpr (WF == kW8) return t * (int64_t)kNTile * k + j * (2 * kChunkBytes);
+    else return packed_chunk_offset(t, j, k);
+}
+
+// Full 128-wide chunk j of tile t, this lane's record (streamed: nontemporal).
+template <int WF>
+__device__ __forceinline__ WRec<WF> load_wrec(const uint8_t *w, int64_t t, int64_t j,
+                                              int64_t k, int lane) {
+    const uint8_t *base = w + wchunk_offset<WF>(t, j, k) + lane * 16;
+    WRec<WF> rec;
+    if constexpr (WF == kW8) {
+        rec.r0 = __builtin_nontemporal_load((const u32x4 *)base);
+        rec.r1 = __builtin_nontemporal_load((const u32x4 *)(base + kChunkBytes));
+    } else {
+        rec.r = __builtin_nontemporal_load((const u32x4 *)base);
+    }
+    return rec;
+}
+
+// Trailing 64-wide chunk j of tile t (step 0 only).
+template <int WF>
+__device__ __forceinline__ WRec<WF> load_wrec_half(const uint8_t *w, int64_t t, int64_t j,
+                                                   int64_t k, int lane) {
+    WRec<WF> rec;
+    if constexpr (WF == kW8) {
+        rec.r0 = *(const u32x4 *)(w + wchunk_offset<WF>(t, j, k) + lane * 16);
+        rec.r1 = rec.r0;
+    } else {
+        const u32x2 h = *(const u32x2 *)(w + wchunk_offset<WF>(t, j, k) + lane * 8);
+        rec.r = u32x4{h.x, h.y, 0u, 0u};
+    }
+    return rec;
+}
+
+// The 16-byte int8 operand of K step h (0 or 1) from a record and the step's
+// group parameter.
+template <int WF>
+__device__ __forceinline__ v4i wrec_operand(const WRec<WF> &rec, int h, uint32_t param) {
+    if constexpr (WF == kW8) {
+        return __builtin_bit_cast(v4i, h ? rec.r1 : rec.r0);
+    } else {
+        uint32_t mul, add;
+        if constexpr (WF == kW4Lqq) {
+            const uint32_t s = param & 0xffu, a = param >> 8;
+            mul = s | (s << 16);
+            add = a * 0x01010101u;
+        } else {
+            scale_consts(param, mul, add);
+        }
+        return unpack_step(h ? rec.r.z : rec.r.x, h ? rec.r.w : rec.r.y, mul, add);
+    }
+}
+
 }  // namespace w4a8

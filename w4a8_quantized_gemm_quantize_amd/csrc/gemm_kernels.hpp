@@ -1,6 +1,9 @@
-// gemm.hip -- W4A8 GEMM for gfx950: int8 activations x packed 4-bit weights,
-// int8 MFMA with exact int32 accumulation, integer group scales folded into
-// the int8 weight operand, binary32 / bf16 / int32 epilogue.
+// gemm_kernels.hpp -- W4A8 GEMM kernels for gfx950: int8 activations x packed
+// 4-bit weights, int8 MFMA with exact int32 accumulation, integer group scales
+// folded into the int8 weight operand, binary32 / bf16 / int32 epilogue.  The
+// kernels are templates over the weight format (device_common.hpp: symmetric
+// 4-bit, LQQ 4-bit, or int8 for the W8A8 comparison path); gemm_w4.hip,
+// gemm_lqq.hip and gemm_w8.hip instantiate one format each.
 //
 // Method: "LiquidGEMM" verdict page (pith.science arXiv 2509.01229),
 // referee_report.summary -- 4-bit weights are rebuilt to INT8 inside the kernel
@@ -37,6 +40,8 @@
 //                       rebuilt int8 weight operands in double-buffered LDS,
 //                       one K chunk (128) per barrier; each 16-channel weight
 //                       tile is rebuilt once per workgroup, by one wavefront.
+#pragma once
+
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -71,15 +76,15 @@ __device__ __forceinline__ void store4(void *out, int out_dtype, int64_t row, in
 // ---------------------------------------------------------------- skinny --
 constexpr int kSkinnyMaxVec = 16;   // fused prologue: 16-byte vectors held per thread
 
-template <int NT, int D, int MT, bool WITH_ACT>
+template <int WF, int NT, int D, int MT, bool WITH_ACT>
 struct WeightBatch {
-    u32x4 w[D][NT];                       // one packed record per chunk and tile
-    uint32_t s[D][NT][2];                 // group scales of the chunk's two K steps
+    WRec<WF> w[D][NT];                    // one packed record per chunk and tile
+    uint32_t s[D][NT][2];                 // group parameters of the chunk's two K steps
     v4i a[WITH_ACT ? D : 1][2][MT];       // int8 activation fragments (non-fused)
 };
 
 // AV: 16-byte activation vectors per thread in the fused prologue (unused otherwise).
-template <int MT, int NT, int WAVES, int D, bool FUSED, int AV>
+template <int WF, int MT, int NT, int WAVES, int D, bool FUSED, int AV>
 __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     const void *__restrict__ act, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ w_packed, const uint8_t *__restrict__ grp_scale,
@@ -121,18 +126,17 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     // is never used (chunks are skipped, rows masked at use, tiles not stored).
     // A branch around a load would make the compiler wait for it at the join.
     const int64_t tlast = ntiles - 1;
-    auto load_batch = [&](WeightBatch<NT, D, MT, !FUSED> &b, int64_t jb) {
+    auto load_batch = [&](WeightBatch<WF, NT, D, MT, !FUSED> &b, int64_t jb) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int64_t j = (jb + d < j1) ? jb + d : j1 - 1;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 const int64_t t = (t0 + nt < ntiles) ? t0 + nt : tlast;
-                const uint8_t *sg = grp_scale + t * kNTile * G + (2 * j) * kNTile + c;
-                b.w[d][nt] = __builtin_nontemporal_load(
-                    (const u32x4 *)(w_packed + packed_chunk_offset(t, j, k)) + lane);
-                b.s[d][nt][0] = sg[0];
-                b.s[d][nt][1] = sg[kNTile];
+                const int64_t pidx = t * kNTile * G + (2 * j) * kNTile + c;
+                b.w[d][nt] = load_wrec<WF>(w_packed, t, j, k, lane);
+                b.s[d][nt][0] = load_wparam<WF>(grp_scale, pidx);
+                b.s[d][nt][1] = load_wparam<WF>(grp_scale, pidx + kNTile);
             }
             if constexpr (!FUSED) {
 #pragma unroll
@@ -147,7 +151,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
         }
     };
 
-    WeightBatch<NT, D, MT, !FUSED> cur;
+    WeightBatch<WF, NT, D, MT, !FUSED> cur;
     if constexpr (!FUSED) {
         if (j0 < j1) load_batch(cur, j0);
         __syncthreads();  // red cleared
@@ -236,12 +240,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 
     // One K step (64) of one chunk: rebuild the weight operand of each tile and
     // multiply it into every row tile.
-    auto mma_step = [&](const u32x2 wp[NT], const uint32_t sv[NT], const v4i av[MT]) {
+    auto mma_step = [&](const WRec<WF> rec[NT], int h, const uint32_t sv[NT],
+                        const v4i av[MT]) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            uint32_t mul, add;
-            scale_consts(sv[nt], mul, add);
-            const v4i wv = unpack_step(wp[nt].x, wp[nt].y, mul, add);
+            const v4i wv = wrec_operand<WF>(rec[nt], h, sv[nt]);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = mfma16x16x64(wv, av[mt], acc[nt][mt]);
         }
@@ -262,7 +265,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     };
 
     for (int64_t jb = j0; jb < j1; jb += D) {
-        WeightBatch<NT, D, MT, !FUSED> nxt;
+        WeightBatch<WF, NT, D, MT, !FUSED> nxt;
         if (jb + D < j1) load_batch(nxt, jb + D);
 #pragma unroll
         for (int d = 0; d < D; ++d) {
@@ -270,14 +273,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
             if (j >= j1) break;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                u32x2 wp[NT];
                 uint32_t sv[NT];
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    wp[nt] = h ? u32x2{cur.w[d][nt].z, cur.w[d][nt].w}
-                               : u32x2{cur.w[d][nt].x, cur.w[d][nt].y};
-                    sv[nt] = cur.s[d][nt][h];
-                }
+                for (int nt = 0; nt < NT; ++nt) sv[nt] = cur.s[d][nt][h];
                 v4i av[MT];
                 if constexpr (FUSED) {
                     lds_act(av, j * kChunkK + h * kGroup + kq * 16);
@@ -286,22 +284,22 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
                     for (int mt = 0; mt < MT; ++mt) av[mt] = cur.a[d][h][mt];
                 }
                 mask_rows(av);
-                mma_step(wp, sv, av);
+                mma_step(cur.w[d], h, sv, av);
             }
         }
         cur = nxt;
     }
 
     if (has_half && wave == WAVES - 1) {
-        // Trailing 64-wide chunk: 8-byte lane records, one K step.
+        // Trailing 64-wide chunk: one K step.
         const int64_t j = nfull;
-        u32x2 wp[NT];
+        WRec<WF> wp[NT];
         uint32_t sv[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int64_t t = (t0 + nt < ntiles) ? t0 + nt : tlast;
-            wp[nt] = *((const u32x2 *)(w_packed + packed_chunk_offset(t, j, k)) + lane);
-            sv[nt] = grp_scale[t * kNTile * G + (2 * j) * kNTile + c];
+            wp[nt] = load_wrec_half<WF>(w_packed, t, j, k, lane);
+            sv[nt] = load_wparam<WF>(grp_scale, t * kNTile * G + (2 * j) * kNTile + c);
         }
         v4i av[MT];
         const int64_t kk = j * kChunkK + kq * 16;
@@ -315,7 +313,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
             }
         }
         mask_rows(av);
-        mma_step(wp, sv, av);
+        mma_step(wp, 0, sv, av);
     }
 
 #pragma unroll
@@ -368,7 +366,7 @@ __device__ __forceinline__ int act_lds_off(int row, int c16) {
     return row * kChunkK + (act_swz(row, c16) << 4);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+template <int WF, int BM, int BN, int WAVES_M, int WAVES_N>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
     const int8_t *__restrict__ a_q, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ w_packed, const uint8_t *__restrict__ grp_scale,
@@ -436,48 +434,54 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
             global_to_lds16(a_q + gm * k + j * kChunkK + c16 * 16, base + blk * 1024);
         }
     };
-    // Packed records and group scales of this wavefront's tile(s) for chunk j:
-    // exactly three loads per tile whatever the chunk (the waits below count
-    // them).  Tiles past n are clamped to the last tile (outputs not stored).
-    // A trailing 64-wide chunk has 8-byte records: the 16-byte window is
-    // clamped inside the 512-byte chunk and the wanted half picked after the
-    // load; its missing second group reuses the first group's scale.
-    u32x4 wrec[TPW];
+    // Packed records and group parameters of this wavefront's tile(s) for
+    // chunk j, with a fixed number of unconditional loads whatever the chunk.
+    // Tiles past n are clamped to the last tile (outputs not stored).  A
+    // trailing 64-wide chunk of a 4-bit format has 8-byte records: the 16-byte
+    // window is clamped inside the 512-byte chunk and the wanted half picked
+    // after the load; its missing second group reuses the first group's
+    // parameter.  An int8 half chunk holds step 0 only, whose address is
+    // reloaded in place of step 1.
+    WRec<WF> wrec[TPW];
     uint32_t wsc[TPW][2];
     bool wfull = true;
     auto fetch_w = [&](int64_t j) {
         wfull = (j + 1) * kChunkK <= k;
-        const int rec_off = wfull ? lane * 16 : (lane * 8 < 496 ? lane * 8 : 496);
         const int64_t g1 = wfull ? 2 * j + 1 : 2 * j;
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const int64_t t = (t0 + wave * TPW + i < ntiles) ? t0 + wave * TPW + i : ntiles - 1;
-            const uint8_t *sg = grp_scale + t * kNTile * G + c;
-            wrec[i] = *(const u32x4 *)(w_packed + packed_chunk_offset(t, j, k) + rec_off);
-            wsc[i][0] = sg[(2 * j) * kNTile];
-            wsc[i][1] = sg[g1 * kNTile];
+            if constexpr (WF == kW8) {
+                const uint8_t *base = w_packed + wchunk_offset<WF>(t, j, k) + lane * 16;
+                wrec[i].r0 = *(const u32x4 *)base;
+                wrec[i].r1 = *(const u32x4 *)(wfull ? base + kChunkBytes : base);
+                wsc[i][0] = wsc[i][1] = 0u;
+            } else {
+                const int rec_off = wfull ? lane * 16 : (lane * 8 < 496 ? lane * 8 : 496);
+                wrec[i].r = *(const u32x4 *)(w_packed + packed_chunk_offset(t, j, k) + rec_off);
+                wsc[i][0] = load_wparam<WF>(grp_scale, t * kNTile * G + (2 * j) * kNTile + c);
+                wsc[i][1] = load_wparam<WF>(grp_scale, t * kNTile * G + g1 * kNTile + c);
+            }
         }
     };
     // Rebuild the int8 operands of both K steps into stage buf.
     auto rebuild_w = [&](auto buf_tag) {
         uint8_t *wbase = decltype(buf_tag)::value ? wl1 : wl0;
-        if (!wfull) {
+        if constexpr (WF != kW8) {
+            if (!wfull) {
 #pragma unroll
-            for (int i = 0; i < TPW; ++i)
-                wrec[i] = (lane == 63) ? u32x4{wrec[i].z, wrec[i].w, 0u, 0u}
-                                       : u32x4{wrec[i].x, wrec[i].y, 0u, 0u};
+                for (int i = 0; i < TPW; ++i)
+                    wrec[i].r = (lane == 63) ? u32x4{wrec[i].r.z, wrec[i].r.w, 0u, 0u}
+                                             : u32x4{wrec[i].r.x, wrec[i].r.y, 0u, 0u};
+            }
         }
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const int tt = wave * TPW + i;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                uint32_t mul, add;
-                scale_consts(wsc[i][h], mul, add);
-                const v4i wv = unpack_step(h ? wrec[i].z : wrec[i].x, h ? wrec[i].w : wrec[i].y,
-                                           mul, add);
-                *(v4i *)(wbase + ((tt * 2 + h) * 64 + lane) * 16) = wv;
-            }
+            for (int h = 0; h < 2; ++h)
+                *(v4i *)(wbase + ((tt * 2 + h) * 64 + lane) * 16) =
+                    wrec_operand<WF>(wrec[i], h, wsc[i][h]);
         }
     };
 
@@ -622,7 +626,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
     }
 }
 
-template <int MT, int NT, bool FUSED, int AV = 1>
+template <int WF, int MT, int NT, bool FUSED, int AV = 1>
 void launch_skinny(const void *act, const float *a_scale, const uint8_t *w_packed,
                    const uint8_t *grp_scale, const float *ch_scale, int64_t m, int64_t n,
                    int64_t k, void *out, int out_dtype, int8_t *ws_q, float *ws_s,
@@ -631,17 +635,17 @@ void launch_skinny(const void *act, const float *a_scale, const uint8_t *w_packe
     constexpr int WAVES = 8, D = FUSED ? 4 : (MT == 1 ? 4 : (MT == 2 ? 2 : 1));
     const int64_t ntiles = n / kNTile;
     const unsigned grid = (unsigned)((ntiles + NT - 1) / NT);
-    gemm_skinny_kernel<MT, NT, WAVES, D, FUSED, AV><<<grid, 64 * WAVES, dyn_lds, stream>>>(
+    gemm_skinny_kernel<WF, MT, NT, WAVES, D, FUSED, AV><<<grid, 64 * WAVES, dyn_lds, stream>>>(
         act, a_scale, w_packed, grp_scale, ch_scale, (int)m, n, k, out, out_dtype, ws_q, ws_s);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+template <int WF, int BM, int BN, int WAVES_M, int WAVES_N>
 void launch_tiled(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
                   const uint8_t *grp_scale, const float *ch_scale, int64_t m, int64_t n,
                   int64_t k, void *out, int out_dtype, hipStream_t stream) {
     const int64_t grid = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-    gemm_tiled_kernel<BM, BN, WAVES_M, WAVES_N><<<(unsigned)grid, 64 * WAVES_M * WAVES_N, 0,
-                                                  stream>>>(
+    gemm_tiled_kernel<WF, BM, BN, WAVES_M, WAVES_N><<<(unsigned)grid, 64 * WAVES_M * WAVES_N,
+                                                      0, stream>>>(
         a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out, out_dtype);
 }
 
@@ -660,38 +664,41 @@ int fused_vectors(int64_t m, int64_t k) {
     return need <= 4 ? 4 : need <= 8 ? 8 : need <= kSkinnyMaxVec ? 16 : 0;
 }
 
-}  // namespace
-
-hipError_t launch_w4a8_gemm(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
+// GEMM on int8 activations for weight format WF.
+template <int WF>
+hipError_t launch_gemm_fmt(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
                             const uint8_t *grp_scale, const float *ch_scale, int64_t m,
                             int64_t n, int64_t k, void *out, int out_dtype,
                             hipStream_t stream) {
     if (m == 0 || n == 0) return hipSuccess;
     const int64_t ntiles = n / kNTile;
     if (m <= 16) {
-        launch_skinny<1, 1, false>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out,
+        launch_skinny<WF, 1, 1, false>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out,
                                    out_dtype, nullptr, nullptr, 0, stream);
     } else if (m <= 32) {
-        launch_skinny<2, 1, false>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out,
+        launch_skinny<WF, 2, 1, false>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out,
                                    out_dtype, nullptr, nullptr, 0, stream);
     } else if (m <= 64) {
         if (ntiles >= 512)
-            launch_skinny<4, 2, false>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k,
+            launch_skinny<WF, 4, 2, false>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k,
                                        out, out_dtype, nullptr, nullptr, 0, stream);
         else
-            launch_skinny<4, 1, false>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k,
+            launch_skinny<WF, 4, 1, false>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k,
                                        out, out_dtype, nullptr, nullptr, 0, stream);
     } else if (m <= 128) {
-        launch_tiled<128, 128, 2, 2>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out,
+        launch_tiled<WF, 128, 128, 2, 2>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out,
                                out_dtype, stream);
     } else {
-        launch_tiled<256, 256, 4, 4>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out,
+        launch_tiled<WF, 256, 256, 4, 4>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out,
                                out_dtype, stream);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_w4a8_gemm_bf16act(const uint16_t *a, const uint8_t *w_packed,
+// Per-token quantization of bf16 activations into (ws_q, ws_s) and the GEMM;
+// small m runs both in one kernel.
+template <int WF>
+hipError_t launch_gemm_bf16act_fmt(const uint16_t *a, const uint8_t *w_packed,
                                     const uint8_t *grp_scale, const float *ch_scale, int64_t m,
                                     int64_t n, int64_t k, void *out, int out_dtype,
                                     int8_t *ws_q, float *ws_s, hipStream_t stream) {
@@ -700,20 +707,21 @@ hipError_t launch_w4a8_gemm_bf16act(const uint16_t *a, const uint8_t *w_packed,
     if (av > 0) {
         const size_t lds_bytes = (size_t)(m * (k + 16));
         if (av == 4)
-            launch_skinny<1, 1, true, 4>(a, nullptr, w_packed, grp_scale, ch_scale, m, n, k, out,
+            launch_skinny<WF, 1, 1, true, 4>(a, nullptr, w_packed, grp_scale, ch_scale, m, n, k, out,
                                          out_dtype, ws_q, ws_s, lds_bytes, stream);
         else if (av == 8)
-            launch_skinny<1, 1, true, 8>(a, nullptr, w_packed, grp_scale, ch_scale, m, n, k, out,
+            launch_skinny<WF, 1, 1, true, 8>(a, nullptr, w_packed, grp_scale, ch_scale, m, n, k, out,
                                          out_dtype, ws_q, ws_s, lds_bytes, stream);
         else
-            launch_skinny<1, 1, true, 16>(a, nullptr, w_packed, grp_scale, ch_scale, m, n, k,
+            launch_skinny<WF, 1, 1, true, 16>(a, nullptr, w_packed, grp_scale, ch_scale, m, n, k,
                                           out, out_dtype, ws_q, ws_s, lds_bytes, stream);
         return hipGetLastError();
     }
     hipError_t e = launch_quantize_act(a, m, k, (int32_t)k, ws_q, ws_s, stream);
     if (e != hipSuccess) return e;
-    return launch_w4a8_gemm(ws_q, ws_s, w_packed, grp_scale, ch_scale, m, n, k, out, out_dtype,
-                            stream);
+    return launch_gemm_fmt<WF>(ws_q, ws_s, w_packed, grp_scale, ch_scale, m, n, k, out,
+                               out_dtype, stream);
 }
 
+}  // namespace
 }  // namespace w4a8

@@ -26,4 +26,34 @@ hipError_t launch_w4a8_gemm_bf16act(const uint16_t *a, const uint8_t *w_packed,
                                     int64_t n, int64_t k, void *out, int out_dtype,
                                     int8_t *ws_q, float *ws_s, hipStream_t stream);
 
+
+// LiquidGEMM's asymmetric LQQ weights (parameter s | (128 + min) << 8 per group).
+hipError_t launch_pack_w4_lqq(const uint16_t *w, int64_t n, int64_t k, uint8_t *w_packed,
+                              uint16_t *grp_param, float *ch_scale, hipStream_t stream);
+hipError_t launch_unpack_w4_lqq(const uint8_t *w_packed, const uint16_t *grp_param, int64_t n,
+                                int64_t k, uint8_t *q_u4, uint8_t *s_u8, int8_t *w_min,
+                                hipStream_t stream);
+hipError_t launch_w4a8_gemm_lqq(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
+                                const uint16_t *grp_param, const float *ch_scale, int64_t m,
+                                int64_t n, int64_t k, void *out, int out_dtype,
+                                hipStream_t stream);
+hipError_t launch_w4a8_gemm_lqq_bf16act(const uint16_t *a, const uint8_t *w_packed,
+                                        const uint16_t *grp_param, const float *ch_scale,
+                                        int64_t m, int64_t n, int64_t k, void *out,
+                                        int out_dtype, int8_t *ws_q, float *ws_s,
+                                        hipStream_t stream);
+
+// W8A8 comparison path: per-channel int8 weights in the kW8 layout.
+hipError_t launch_pack_w8(const uint16_t *w, int64_t n, int64_t k, int8_t *w_packed,
+                          float *ch_scale, hipStream_t stream);
+hipError_t launch_unpack_w8(const int8_t *w_packed, int64_t n, int64_t k, int8_t *q8,
+                            hipStream_t stream);
+hipError_t launch_w8a8_gemm(const int8_t *a_q, const float *a_scale, const int8_t *w_packed,
+                            const float *ch_scale, int64_t m, int64_t n, int64_t k, void *out,
+                            int out_dtype, hipStream_t stream);
+hipError_t launch_w8a8_gemm_bf16act(const uint16_t *a, const int8_t *w_packed,
+                                    const float *ch_scale, int64_t m, int64_t n, int64_t k,
+                                    void *out, int out_dtype, int8_t *ws_q, float *ws_s,
+                                    hipStream_t stream);
+
 }  // namespace w4a8
