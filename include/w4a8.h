@@ -273,6 +273,29 @@ w4a8_status w8a8_gemm_bf16act(const uint16_t *a, const int8_t *w_packed, const f
                               int64_t m, int64_t n, int64_t k, void *out, w4a8_dtype out_dtype,
                               void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * EQuARX receive step ("EQuARX" verdict page, pith_extraction.key_machinery:
+ * a block-quantized int8 shard is dequantized to FP32 before it is added to
+ * the local partial sum, and the sum is block-quantized again for the next
+ * hop of the ring).  The single-GPU local step of that reduction.
+ * ------------------------------------------------------------------------ */
+
+/*
+ *   q_in    [rows, cols] int8 and s_in [rows, cols/block] binary32: the
+ *           received block-quantized shard
+ *   x       [rows, cols] local partial sum: binary32 (x_dtype W4A8_F32) or
+ *           bf16 bits (W4A8_BF16)
+ *   sum_out [rows, cols] binary32, may be NULL: v = fl(x + fl(q_in * s_in))
+ *   q_out, s_out: quantize_act_blockwise of v (same block, same rounding:
+ *           s = amax / 127, q = rne(v * (127 / amax)) in [-127, 127])
+ * Shape rules as for quantize_act_blockwise; x_dtype W4A8_I32 is
+ * W4A8_ERR_UNSUPPORTED.  q_out may not alias q_in; sum_out may not alias x.
+ */
+w4a8_status dequant_add_requant(const int8_t *q_in, const float *s_in, const void *x,
+                                w4a8_dtype x_dtype, int64_t rows, int64_t cols, int32_t block,
+                                float *sum_out, int8_t *q_out, float *s_out,
+                                hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

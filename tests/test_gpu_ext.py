@@ -1,5 +1,6 @@
 """GPU parity of the extension paths with the CPU oracle, through the C ABI:
-LQQ (LiquidGEMM's asymmetric 4-bit weights) and the W8A8 comparison path.
+LQQ (LiquidGEMM's asymmetric 4-bit weights), the W8A8 comparison path and the
+EQuARX dequantize-add-requantize step.
 
 Same bar as the main path: codes, scales, group parameters and raw int32
 accumulators bit-exact; binary32 outputs within 1e-5 relative; bf16 outputs
@@ -183,3 +184,62 @@ def test_w8a8_float_outputs_and_fused(w4a8, m, n, k):
     assert_f32_close(y32.cpu().numpy(), y_ref)
     assert_bf16_within_ulp(bits_of(y16), y_ref)
     assert torch.equal(yf.view(torch.int32), y32.view(torch.int32))
+
+
+# ------------------------------------------------------ EQuARX receive step --
+
+@pytest.mark.parametrize("rows,cols,block,xtype,want_sum", [
+    (64, 1024, 32, "f32", True),
+    (64, 1024, 128, "bf16", False),
+    (7, 4096, 8, "f32", False),
+    (33, 512, 512, "bf16", True),
+    (5, 96, 24, "f32", True),        # non-power-of-two block: one workgroup per block
+    (3, 8192, 8192, "bf16", True),   # one block per row, longer than the register window
+    (1024, 2048, 64, "bf16", False),
+])
+def test_dequant_add_requant_matches_oracle(w4a8, rows, cols, block, xtype, want_sum):
+    announce("equarx step", rows, cols, block, xtype, want_sum)
+    q_in, s_in = oracle.quantize_act_blockwise(inputs.activations(rows, cols, seed=rows), block)
+    xb = inputs.activations(rows, cols, seed=rows + 1, outlier_frac=0.001)
+    if xtype == "f32":
+        x = (xb.astype(np.uint32) << 16).view(np.float32) * np.float32(0.37)
+        x[0, :block] = -(q_in[0, :block].astype(np.float32) * s_in[0, 0])   # a block summing to 0
+        x_dev = torch.from_numpy(x).cuda()
+    else:
+        x = xb
+        x_dev = to_dev_bf16(xb)
+    q, s, v = w4a8.dequant_add_requant(torch.from_numpy(q_in).cuda(),
+                                       torch.from_numpy(s_in).cuda(), x_dev, block,
+                                       want_sum=want_sum)
+    torch.cuda.synchronize()
+    q_ref, s_ref, v_ref = oracle.dequant_add_requant(q_in, s_in, x, block)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    if want_sum:
+        assert np.array_equal(v.cpu().numpy().view(np.uint32), v_ref.view(np.uint32))
+    if xtype == "f32":
+        assert s_ref[0, 0] == 0 and (q_ref[0, :block] == 0).all()
+
+
+def test_dequant_add_requant_64m_workload(w4a8):
+    # the standalone quantizer's size: 64M elements, as one ring step would see it
+    rows, cols, block = 65536, 1024, 32
+    announce("equarx step 64M", rows, cols, block)
+    q_in, s_in = oracle.quantize_act_blockwise(inputs.activations(rows, cols, seed=4), block)
+    xb = inputs.activations(rows, cols, seed=5)
+    q, s, _ = w4a8.dequant_add_requant(torch.from_numpy(q_in).cuda(),
+                                       torch.from_numpy(s_in).cuda(), to_dev_bf16(xb), block)
+    torch.cuda.synchronize()
+    q_ref, s_ref, _ = oracle.dequant_add_requant(q_in, s_in, xb, block, want_sum=False)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+def test_dequant_add_requant_argument_errors(w4a8):
+    q = torch.zeros((4, 64), dtype=torch.int8, device="cuda")
+    s = torch.zeros((4, 2), dtype=torch.float32, device="cuda")
+    x = torch.zeros((4, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(w4a8.W4A8Error):
+        w4a8.dequant_add_requant(q, s, x, 48)          # 64 % 48 != 0
+    with pytest.raises(w4a8.W4A8Error):
+        w4a8.dequant_add_requant(q, s, x, 12)          # block % 8 != 0

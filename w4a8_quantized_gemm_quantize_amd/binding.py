@@ -56,6 +56,8 @@ _SIGS = {
     "w8a8_gemm": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P], ctypes.c_int),
     "w8a8_gemm_bf16act": ([_P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P, ctypes.c_size_t,
                            _P], ctypes.c_int),
+    "dequant_add_requant": ([_P, _P, _P, ctypes.c_int, _I64, _I64, _I32, _P, _P, _P, _P],
+                            ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -317,3 +319,31 @@ def w8a8_gemm_bf16act(a, w_packed, ch_scale, n: int, out_dtype=torch.bfloat16, o
                                   _OUT[out.dtype], _ptr(workspace), workspace.numel(),
                                   _stream(stream)))
     return out
+
+
+# ---------------------------------------------------- EQuARX receive step --
+
+def dequant_add_requant(q_in, s_in, x, block: int, want_sum: bool = False, q_out=None,
+                        s_out=None, sum_out=None, stream=None):
+    """(q_in int8 [r, c], s_in f32 [r, c/block]) + x (float32 or bfloat16 [r, c])
+    -> (q_out int8, s_out f32, sum f32 or None): requantized per block."""
+    _dev(q_in, torch.int8, "q_in")
+    _dev(s_in, torch.float32, "s_in")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("x must be float32 or bfloat16")
+    _dev(x, x.dtype, "x")
+    rows, cols = q_in.shape
+    dev = q_in.device
+    if q_out is None:
+        q_out = torch.empty((rows, cols), dtype=torch.int8, device=dev)
+    if s_out is None:
+        s_out = torch.empty((rows, cols // block if block > 0 else 0), dtype=torch.float32,
+                            device=dev)
+    if want_sum and sum_out is None:
+        sum_out = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+    _check("dequant_add_requant",
+           _lib.dequant_add_requant(_ptr(q_in), _ptr(s_in), _ptr(x),
+                                    BF16 if x.dtype == torch.bfloat16 else F32, rows, cols,
+                                    block, _ptr(sum_out), _ptr(q_out), _ptr(s_out),
+                                    _stream(stream)))
+    return q_out, s_out, sum_out

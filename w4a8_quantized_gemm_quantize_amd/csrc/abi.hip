@@ -304,4 +304,23 @@ w4a8_status w8a8_gemm_bf16act(const uint16_t *a, const int8_t *w_packed, const f
                   stream);
 }
 
+/* ------------------------------------------------- EQuARX receive step */
+
+w4a8_status dequant_add_requant(const int8_t *q_in, const float *s_in, const void *x,
+                                w4a8_dtype x_dtype, int64_t rows, int64_t cols, int32_t block,
+                                float *sum_out, int8_t *q_out, float *s_out,
+                                hipStream_t stream) {
+    w4a8_status st = check_act_shape(rows, cols, block);
+    if (st != W4A8_OK) return st;
+    if (x_dtype != W4A8_F32 && x_dtype != W4A8_BF16) return W4A8_ERR_UNSUPPORTED;
+    if (rows == 0 || cols == 0) return W4A8_OK;
+    if (!q_in || !s_in || !x || !q_out || !s_out) return W4A8_ERR_NULL;
+    if (!aligned16(q_in) || !aligned16(s_in) || !aligned16(x) || !aligned16(q_out) ||
+        !aligned16(s_out) || (sum_out && !aligned16(sum_out)))
+        return W4A8_ERR_MISALIGNED;
+    return finish(w4a8::launch_dequant_add_requant(q_in, s_in, x, x_dtype == W4A8_BF16, rows,
+                                                   cols, block, sum_out, q_out, s_out, stream),
+                  stream);
+}
+
 }  // extern "C"

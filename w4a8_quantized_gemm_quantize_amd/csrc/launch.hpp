@@ -56,4 +56,10 @@ hipError_t launch_w8a8_gemm_bf16act(const uint16_t *a, const int8_t *w_packed,
                                     void *out, int out_dtype, int8_t *ws_q, float *ws_s,
                                     hipStream_t stream);
 
+// EQuARX receive step: requantize(dequantize(q_in, s_in) + x) per block.
+hipError_t launch_dequant_add_requant(const int8_t *q_in, const float *s_in, const void *x,
+                                      bool x_bf16, int64_t rows, int64_t cols, int32_t block,
+                                      float *sum_out, int8_t *q_out, float *s_out,
+                                      hipStream_t stream);
+
 }  // namespace w4a8
