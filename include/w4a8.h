@@ -274,6 +274,36 @@ w4a8_status w8a8_gemm_bf16act(const uint16_t *a, const int8_t *w_packed, const f
                               void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Per-block activation scales inside the GEMM: activations quantized by
+ * quantize_act_blockwise with blocks of 32, 64 or 128 along K ("EQuARX"
+ * verdict page, pith_extraction.key_machinery: one FP32 scale per block) feed
+ * the W4A8 GEMM directly; the block scales are applied per K-group as the
+ * int32 partials come out of the matrix cores.
+ * ------------------------------------------------------------------------ */
+
+/*
+ *   a_q      [m, k] int8, a_scale [m, k / block] binary32 (quantize_act_blockwise
+ *            output with the same block)
+ *   w_packed, grp_scale, ch_scale: as written by pack_w4_grouped
+ *   out      [m, n] binary32 (W4A8_F32) or bf16 (W4A8_BF16); W4A8_I32 is
+ *            W4A8_ERR_UNSUPPORTED
+ * For each activation block b (k in [b * block, (b + 1) * block)):
+ *   P_b[m, n] = sum_{k in b} a_q[m, k] * q[n, k] * s_g[n, k / 64]   (int32, exact)
+ * and, in binary32 with one rounding per operation and blocks in increasing
+ * order (the order within one block's row of a wavefront's K range; ranges of
+ * different wavefronts may be summed in another order):
+ *   f = 0;  f = f + P_b * a_scale[m, b]  for each b;   out = f * ch_scale[n].
+ * The error against the exact value is at most about (k / block + 2) * 2^-24
+ * times sum_b |a_scale[m, b] * P_b| * ch_scale[n].
+ * block must be 32, 64 or 128 (else W4A8_ERR_UNSUPPORTED) and divide k
+ * (W4A8_ERR_SHAPE); otherwise the w4a8_gemm rules apply.
+ */
+w4a8_status w4a8_gemm_blockact(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
+                               const uint8_t *grp_scale, const float *ch_scale, int64_t m,
+                               int64_t n, int64_t k, int32_t group, int32_t block, void *out,
+                               w4a8_dtype out_dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * EQuARX receive step ("EQuARX" verdict page, pith_extraction.key_machinery:
  * a block-quantized int8 shard is dequantized to FP32 before it is added to
  * the local partial sum, and the sum is block-quantized again for the next

@@ -1,6 +1,7 @@
 """GPU parity of the extension paths with the CPU oracle, through the C ABI:
-LQQ (LiquidGEMM's asymmetric 4-bit weights), the W8A8 comparison path and the
-EQuARX dequantize-add-requantize step.
+LQQ (LiquidGEMM's asymmetric 4-bit weights), the W8A8 comparison path, the
+EQuARX dequantize-add-requantize step and the GEMM with per-block activation
+scales (a binary32 fold, checked against the error bound that fold implies).
 
 Same bar as the main path: codes, scales, group parameters and raw int32
 accumulators bit-exact; binary32 outputs within 1e-5 relative; bf16 outputs
@@ -243,3 +244,76 @@ def test_dequant_add_requant_argument_errors(w4a8):
         w4a8.dequant_add_requant(q, s, x, 48)          # 64 % 48 != 0
     with pytest.raises(w4a8.W4A8Error):
         w4a8.dequant_add_requant(q, s, x, 12)          # block % 8 != 0
+
+
+# ---------------------------------------------- per-block activation scales --
+
+def blockact_tolerance(y_ref, bound, nb):
+    """Binary32 evaluation of s_ch * sum_b s_b * P_b: one rounding per product and
+    per addition (at most nb + 8 additions in any order, the wavefronts' partial
+    sums included) and the final multiply: |err| <= (nb + 10) 2^-24 * bound."""
+    return (nb + 10) * 2.0**-24 * bound
+
+
+BLOCKACT_CASES = [
+    (8, 4096, 4096, 32), (8, 4096, 4096, 128),       # decode shape
+    (5, 48, 192, 32), (5, 48, 192, 64),              # trailing half chunk
+    (17, 32, 320, 32), (64, 64, 448, 64),
+    (65, 48, 256, 128),                              # tiled path
+    (200, 272, 384, 32), (200, 272, 384, 64), (200, 272, 384, 128),
+    (129, 144, 4160, 32),
+]
+
+
+@pytest.mark.parametrize("m,n,k,block", BLOCKACT_CASES)
+def test_blockact_gemm_matches_oracle(w4a8, m, n, k, block):
+    announce("blockact gemm", m, n, k, block)
+    w = inputs.weights(n, k, seed=m + n + block)
+    wp, gs, cs = w4a8.pack_w4_grouped(to_dev_bf16(w))
+    q_ref, sg_ref, cs_ref = oracle.quantize_w4_grouped(w, 64)
+    a = inputs.activations(m, k, seed=m + block, outlier_frac=0.001)
+    a_q, a_s = oracle.quantize_act_blockwise(a, block)
+    aq_d, as_d = torch.from_numpy(a_q).cuda(), torch.from_numpy(a_s).cuda()
+    y32 = w4a8.w4a8_gemm_blockact(aq_d, as_d, wp, gs, cs, n, block, out_dtype=torch.float32)
+    y16 = w4a8.w4a8_gemm_blockact(aq_d, as_d, wp, gs, cs, n, block, out_dtype=torch.bfloat16)
+    y32b = w4a8.w4a8_gemm_blockact(aq_d, as_d, wp, gs, cs, n, block, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    y_ref, bound = oracle.w4a8_gemm_blockact(a_q, a_s, q_ref, sg_ref, cs_ref, block)
+    tol = blockact_tolerance(y_ref, bound, k // block)
+    got = y32.cpu().numpy().astype(np.float64)
+    assert (np.abs(got - y_ref) <= tol).all(), float(np.max(np.abs(got - y_ref) / (tol + 1e-300)))
+    got16 = (bits_of(y16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    tol16 = tol + 2.0**-8 * (np.abs(y_ref) + tol)
+    assert (np.abs(got16 - y_ref) <= tol16).all()
+    assert torch.equal(y32.view(torch.int32), y32b.view(torch.int32))    # deterministic
+
+
+def test_blockact_with_equal_block_scales_is_per_token(w4a8):
+    # every block of a row shares one scale: the binary32 fold then carries the
+    # exact integer sums (all below 2^24 here) and must equal the per-token GEMM
+    m, n, k, block = 24, 64, 1024, 64
+    w = inputs.weights(n, k, seed=3)
+    wp, gs, cs = w4a8.pack_w4_grouped(to_dev_bf16(w))
+    rng = np.random.default_rng(3)
+    a_q = rng.integers(-3, 4, size=(m, k), dtype=np.int8)
+    s_row = (2.0 ** rng.integers(-4, 4, size=m)).astype(np.float32)
+    a_s = np.repeat(s_row[:, None], k // block, axis=1).copy()
+    y_blk = w4a8.w4a8_gemm_blockact(torch.from_numpy(a_q).cuda(), torch.from_numpy(a_s).cuda(),
+                                    wp, gs, cs, n, block, out_dtype=torch.float32)
+    y_tok = w4a8.w4a8_gemm(torch.from_numpy(a_q).cuda(), torch.from_numpy(s_row).cuda(), wp, gs,
+                           cs, n, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y_blk, y_tok)
+
+
+def test_blockact_argument_errors(w4a8):
+    a = torch.zeros((4, 192), dtype=torch.int8, device="cuda")
+    s = torch.ones((4, 3), dtype=torch.float32, device="cuda")
+    wp = torch.zeros(16 * 192 // 2, dtype=torch.uint8, device="cuda")
+    gs = torch.ones(16 * 3, dtype=torch.uint8, device="cuda")
+    cs = torch.ones(16, device="cuda")
+    for block in (128, 48, 256):          # 192 % 128 != 0; unsupported block sizes
+        with pytest.raises(w4a8.W4A8Error):
+            w4a8.w4a8_gemm_blockact(a, s, wp, gs, cs, 16, block, out_dtype=torch.float32)
+    with pytest.raises(w4a8.W4A8Error):
+        w4a8.w4a8_gemm_blockact(a, s, wp, gs, cs, 16, 64, out_dtype=torch.int32)

@@ -56,6 +56,8 @@ _SIGS = {
     "w8a8_gemm": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P], ctypes.c_int),
     "w8a8_gemm_bf16act": ([_P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P, ctypes.c_size_t,
                            _P], ctypes.c_int),
+    "w4a8_gemm_blockact": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, ctypes.c_int,
+                            _P], ctypes.c_int),
     "dequant_add_requant": ([_P, _P, _P, ctypes.c_int, _I64, _I64, _I32, _P, _P, _P, _P],
                             ctypes.c_int),
 }
@@ -318,6 +320,23 @@ def w8a8_gemm_bf16act(a, w_packed, ch_scale, n: int, out_dtype=torch.bfloat16, o
            _lib.w8a8_gemm_bf16act(_ptr(a), _ptr(w_packed), _ptr(ch_scale), m, n, k, _ptr(out),
                                   _OUT[out.dtype], _ptr(workspace), workspace.numel(),
                                   _stream(stream)))
+    return out
+
+
+# ------------------------------------------ per-block activation scales GEMM --
+
+def w4a8_gemm_blockact(a_q, a_scale, w_packed, grp_scale, ch_scale, n: int, block: int,
+                       out_dtype=torch.bfloat16, group: int = GROUP, out=None, stream=None):
+    """a_q int8 [m, k], a_scale f32 [m, k / block] -> out [m, n] (float32 or bfloat16)."""
+    _dev(a_q, torch.int8, "a_q")
+    _dev(a_scale, torch.float32, "a_scale")
+    m, k = a_q.shape
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a_q.device)
+    _check("w4a8_gemm_blockact",
+           _lib.w4a8_gemm_blockact(_ptr(a_q), _ptr(a_scale), _ptr(w_packed), _ptr(grp_scale),
+                                   _ptr(ch_scale), m, n, k, group, block, _ptr(out),
+                                   _OUT[out.dtype], _stream(stream)))
     return out
 
 

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libw4a8.so")
-SOURCES = ["abi.hip", "quantize.hip", "pack.hip", "gemm_w4.hip", "gemm_lqq.hip", "gemm_w8.hip", "equarx.hip"]
+SOURCES = ["abi.hip", "quantize.hip", "pack.hip", "gemm_w4.hip", "gemm_lqq.hip", "gemm_w8.hip", "equarx.hip", "gemm_blockact.hip"]
 ARCH = "gfx950"
 
 

@@ -304,6 +304,24 @@ w4a8_status w8a8_gemm_bf16act(const uint16_t *a, const int8_t *w_packed, const f
                   stream);
 }
 
+/* -------------------------------------- per-block activation scales (GEMM) */
+
+w4a8_status w4a8_gemm_blockact(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
+                               const uint8_t *grp_scale, const float *ch_scale, int64_t m,
+                               int64_t n, int64_t k, int32_t group, int32_t block, void *out,
+                               w4a8_dtype out_dtype, hipStream_t stream) {
+    if (block != 32 && block != 64 && block != 128) return W4A8_ERR_UNSUPPORTED;
+    if (out_dtype == W4A8_I32) return W4A8_ERR_UNSUPPORTED;
+    w4a8_status st = check_gemm_args(a_q, a_scale, true, w_packed, grp_scale, ch_scale, m, n,
+                                     k, group, out, out_dtype);
+    if (st != W4A8_OK) return st;
+    if ((k % block) != 0) return W4A8_ERR_SHAPE;
+    if (m == 0 || n == 0) return W4A8_OK;
+    return finish(w4a8::launch_w4a8_gemm_blockact(a_q, a_scale, w_packed, grp_scale, ch_scale, m,
+                                                  n, k, block, out, (int)out_dtype, stream),
+                  stream);
+}
+
 /* ------------------------------------------------- EQuARX receive step */
 
 w4a8_status dequant_add_requant(const int8_t *q_in, const float *s_in, const void *x,

@@ -73,18 +73,56 @@ __device__ __forceinline__ void store4(void *out, int out_dtype, int64_t row, in
     }
 }
 
+// Per-block activation scales (AB > 0): the int32 partial t of one activation
+// block is folded into the binary32 accumulator as f = f + fl(fl(t) * s), block
+// after block in K order.  |t| < 2^24, so fl(t) is exact.
+__device__ __forceinline__ void fold4(f32x4 &f, const v4i t, float s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float p = (float)t[i] * s;
+        f[i] = f[i] + p;
+    }
+}
+
+// Epilogue of the per-block form: out = f * ch_scale, binary32 or bf16.
+__device__ __forceinline__ void store4f(void *out, int out_dtype, int64_t row, int64_t ldo,
+                                        int64_t n, f32x4 f, f32x4 sc) {
+    const int64_t idx = row * ldo + n;
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = f[i] * sc[i];
+    if (out_dtype == 1) {
+        const u32x2 b = {f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16),
+                         f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16)};
+        *(u32x2 *)((uint16_t *)out + idx) = b;
+    } else {
+        *(f32x4 *)((float *)out + idx) = f32x4{y[0], y[1], y[2], y[3]};
+    }
+}
+
+// Activation operand restricted to one 32-wide half of a 64-wide K step: lanes
+// kq = 0, 1 hold k 0..31 of the step, lanes kq = 2, 3 hold k 32..63.
+__device__ __forceinline__ v4i half_operand(v4i a, int kq, int half) {
+    return ((kq >> 1) == half) ? a : v4i{0, 0, 0, 0};
+}
+
 // ---------------------------------------------------------------- skinny --
 constexpr int kSkinnyMaxVec = 16;   // fused prologue: 16-byte vectors held per thread
 
-template <int WF, int NT, int D, int MT, bool WITH_ACT>
+template <int WF, int NT, int D, int MT, bool WITH_ACT, int AB>
 struct WeightBatch {
     WRec<WF> w[D][NT];                    // one packed record per chunk and tile
     uint32_t s[D][NT][2];                 // group parameters of the chunk's two K steps
     v4i a[WITH_ACT ? D : 1][2][MT];       // int8 activation fragments (non-fused)
+    // per-block activation scales of the chunk's K steps (AB > 0): one or two
+    // blocks per step and row tile, for this lane's row
+    float sa[AB ? D : 1][2][AB ? MT : 1][AB == 32 ? 2 : 1];
 };
 
 // AV: 16-byte activation vectors per thread in the fused prologue (unused otherwise).
-template <int WF, int MT, int NT, int WAVES, int D, bool FUSED, int AV>
+// AB: 0 = per-token activation scales a_scale[m]; 32, 64 or 128 = per-block
+// scales a_scale[m][k / AB] folded per block (non-fused form only).
+template <int WF, int MT, int NT, int WAVES, int D, bool FUSED, int AV, int AB = 0>
 __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     const void *__restrict__ act, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ w_packed, const uint8_t *__restrict__ grp_scale,
@@ -94,7 +132,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     constexpr int THREADS = 64 * WAVES;
     constexpr int ROWS = MT * 16;
     extern __shared__ __attribute__((aligned(16))) uint8_t act_lds[];  // FUSED: [m][k + 16]
-    __shared__ int red[NT][16][ROWS + 4];
+    static_assert(AB == 0 || !FUSED, "per-block scales only in the non-fused form");
+    __shared__ int red[AB ? 1 : NT][16][AB ? 1 : ROWS + 4];
+    __shared__ float redf[AB ? WAVES : 1][AB ? NT : 1][16][AB ? ROWS + 1 : 1];
     __shared__ float sa_lds[ROWS];
     __shared__ unsigned amax_lds[ROWS];
 
@@ -107,7 +147,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     const int64_t G = k / kGroup;
     const int64_t lds_stride = k + 16;
 
-    for (int i = tid; i < NT * 16 * (ROWS + 4); i += THREADS) (&red[0][0][0])[i] = 0;
+    if constexpr (AB == 0)
+        for (int i = tid; i < NT * 16 * (ROWS + 4); i += THREADS) (&red[0][0][0])[i] = 0;
+    const int64_t nblk = AB ? k / AB : 1;
     if (tid < ROWS) amax_lds[tid] = 0u;
 
     // Full 128-wide chunks are split evenly over the wavefronts; a trailing
@@ -126,7 +168,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     // is never used (chunks are skipped, rows masked at use, tiles not stored).
     // A branch around a load would make the compiler wait for it at the join.
     const int64_t tlast = ntiles - 1;
-    auto load_batch = [&](WeightBatch<WF, NT, D, MT, !FUSED> &b, int64_t jb) {
+    auto load_batch = [&](WeightBatch<WF, NT, D, MT, !FUSED, AB> &b, int64_t jb) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int64_t j = (jb + d < j1) ? jb + d : j1 - 1;
@@ -146,12 +188,20 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
                         const int row = (mt * 16 + c < m) ? mt * 16 + c : m - 1;
                         b.a[d][h][mt] = *(const v4i *)(a_q + (int64_t)row * k + j * kChunkK +
                                                        h * kGroup + kq * 16);
+                        if constexpr (AB > 0) {
+                            const int64_t ks = 2 * j + h;                  // 64-wide K step
+#pragma unroll
+                            for (int sub = 0; sub < (AB == 32 ? 2 : 1); ++sub) {
+                                const int64_t blk = AB == 32 ? 2 * ks + sub : AB == 64 ? ks : ks / 2;
+                                b.sa[d][h][mt][sub] = a_scale[(int64_t)row * nblk + blk];
+                            }
+                        }
                     }
             }
         }
     };
 
-    WeightBatch<WF, NT, D, MT, !FUSED> cur;
+    WeightBatch<WF, NT, D, MT, !FUSED, AB> cur;
     if constexpr (!FUSED) {
         if (j0 < j1) load_batch(cur, j0);
         __syncthreads();  // red cleared
@@ -233,22 +283,49 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     }
 
     v4i acc[NT][MT];
+    f32x4 accf[AB ? NT : 1][AB ? MT : 1];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = v4i{0, 0, 0, 0};
+        for (int mt = 0; mt < MT; ++mt) {
+            acc[nt][mt] = v4i{0, 0, 0, 0};
+            if constexpr (AB > 0) accf[nt][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
 
     // One K step (64) of one chunk: rebuild the weight operand of each tile and
-    // multiply it into every row tile.
+    // multiply it into every row tile.  With per-block scales (sa: this lane's
+    // row scales of the step's block(s)) each block's partial is folded as
+    // soon as it is complete: per step for blocks of 32 (two half-step
+    // products) and 64, every second step for 128.
+    using SaStep = float[AB ? MT : 1][AB == 32 ? 2 : 1];
     auto mma_step = [&](const WRec<WF> rec[NT], int h, const uint32_t sv[NT],
-                        const v4i av[MT]) {
+                        const v4i av[MT], const SaStep &sa) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const v4i wv = wrec_operand<WF>(rec[nt], h, sv[nt]);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = mfma16x16x64(wv, av[mt], acc[nt][mt]);
+            for (int mt = 0; mt < MT; ++mt) {
+                if constexpr (AB == 0) {
+                    acc[nt][mt] = mfma16x16x64(wv, av[mt], acc[nt][mt]);
+                } else if constexpr (AB == 32) {
+                    const v4i zero = {0, 0, 0, 0};
+                    fold4(accf[nt][mt], mfma16x16x64(wv, half_operand(av[mt], kq, 0), zero),
+                          sa[mt][0]);
+                    fold4(accf[nt][mt], mfma16x16x64(wv, half_operand(av[mt], kq, 1), zero),
+                          sa[mt][AB == 32 ? 1 : 0]);
+                } else if constexpr (AB == 64) {
+                    fold4(accf[nt][mt], mfma16x16x64(wv, av[mt], v4i{0, 0, 0, 0}), sa[mt][0]);
+                } else {
+                    acc[nt][mt] = mfma16x16x64(wv, av[mt], acc[nt][mt]);
+                    if (h == 1) {
+                        fold4(accf[nt][mt], acc[nt][mt], sa[mt][0]);
+                        acc[nt][mt] = v4i{0, 0, 0, 0};
+                    }
+                }
+            }
         }
     };
+    SaStep sa_none = {};
     // Activation fragments of rows mt * 16 + c; rows past m read row m - 1 and
     // are zeroed here.
     auto mask_rows = [&](v4i av[MT]) {
@@ -265,7 +342,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     };
 
     for (int64_t jb = j0; jb < j1; jb += D) {
-        WeightBatch<WF, NT, D, MT, !FUSED> nxt;
+        WeightBatch<WF, NT, D, MT, !FUSED, AB> nxt;
         if (jb + D < j1) load_batch(nxt, jb + D);
 #pragma unroll
         for (int d = 0; d < D; ++d) {
@@ -284,7 +361,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
                     for (int mt = 0; mt < MT; ++mt) av[mt] = cur.a[d][h][mt];
                 }
                 mask_rows(av);
-                mma_step(cur.w[d], h, sv, av);
+                if constexpr (AB > 0) mma_step(cur.w[d], h, sv, av, cur.sa[d][h]);
+                else mma_step(cur.w[d], h, sv, av, sa_none);
             }
         }
         cur = nxt;
@@ -313,9 +391,45 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
             }
         }
         mask_rows(av);
-        mma_step(wp, 0, sv, av);
+        SaStep sa_half = {};
+        if constexpr (AB > 0) {
+            // blocks of 32 or 64 only: k % 128 == 64 excludes blocks of 128
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int row = (mt * 16 + c < m) ? mt * 16 + c : m - 1;
+#pragma unroll
+                for (int sub = 0; sub < (AB == 32 ? 2 : 1); ++sub)
+                    sa_half[mt][sub] =
+                        a_scale[(int64_t)row * nblk + (AB == 32 ? 4 * j + sub : 2 * j)];
+            }
+        }
+        mma_step(wp, 0, sv, av, sa_half);
     }
 
+    if constexpr (AB > 0) {
+        // binary32 partials of each wavefront; summed below in wavefront order
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) redf[wave][nt][4 * kq + i][mt * 16 + c] = accf[nt][mt][i];
+        __syncthreads();
+        for (int idx = tid; idx < NT * m * 4; idx += THREADS) {
+            const int nt = idx / (m * 4);
+            const int rem = idx - nt * m * 4;
+            const int row = rem >> 2, quad = rem & 3;
+            const int64_t t = t0 + nt;
+            if (t >= ntiles) continue;
+            f32x4 f = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int w = 0; w < WAVES; ++w)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) f[i] = f[i] + redf[w][nt][4 * quad + i][row];
+            const int64_t nn = t * kNTile + 4 * quad;
+            store4f(out, out_dtype, row, n, nn, f, *(const f32x4 *)(ch_scale + nn));
+        }
+        return;
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -366,7 +480,9 @@ __device__ __forceinline__ int act_lds_off(int row, int c16) {
     return row * kChunkK + (act_swz(row, c16) << 4);
 }
 
-template <int WF, int BM, int BN, int WAVES_M, int WAVES_N>
+// AB: 0 = per-token activation scales; 32, 64 or 128 = per-block scales
+// a_scale[m][k / AB], each block's int32 partial folded into binary32 in K order.
+template <int WF, int BM, int BN, int WAVES_M, int WAVES_N, int AB = 0>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
     const int8_t *__restrict__ a_q, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ w_packed, const uint8_t *__restrict__ grp_scale,
@@ -486,10 +602,33 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
     };
 
     v4i acc[TN][TM];
+    f32x4 accf[AB ? TN : 1][AB ? TM : 1];
 #pragma unroll
     for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int jj = 0; jj < TM; ++jj) acc[i][jj] = v4i{0, 0, 0, 0};
+        for (int jj = 0; jj < TM; ++jj) {
+            acc[i][jj] = v4i{0, 0, 0, 0};
+            if constexpr (AB > 0) accf[i][jj] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+
+    // Per-block activation scales of this lane's rows for one chunk (AB > 0),
+    // fetched one chunk ahead like the operands.  Blocks past k (a trailing
+    // half chunk) are clamped to the last block and never used.
+    constexpr int NBC = AB ? kChunkK / AB : 1;
+    float scur[AB ? TM : 1][NBC], snxt[AB ? TM : 1][NBC];
+    const int64_t nblk = AB ? k / AB : 1;
+    auto fetch_s = [&](int64_t j, float (&sdst)[AB ? TM : 1][NBC]) {
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+            const int64_t row = m0 + wm * WM + tm * 16 + c;
+            const int64_t rowc = row < m ? row : m - 1;
+#pragma unroll
+            for (int b = 0; b < NBC; ++b) {
+                const int64_t blk = j * NBC + b < nblk ? j * NBC + b : nblk - 1;
+                sdst[tm][b] = a_scale[rowc * nblk + blk];
+            }
+        }
+    };
 
     // One K step (64) of stage buf: LDS reads and MFMAs only.  Activation
     // fragment: lane (c, kq) reads row c of the row tile at 16-byte column
@@ -505,10 +644,42 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
             wv[tn] = *(const v4i *)(wbase + (((wn * TN + tn) * 2 + h) * 64 + lane) * 16);
+        if constexpr (AB == 0) {
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
+            for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-            for (int tm = 0; tm < TM; ++tm) acc[tn][tm] = mfma16x16x64(wv[tn], av[tm], acc[tn][tm]);
+                for (int tm = 0; tm < TM; ++tm)
+                    acc[tn][tm] = mfma16x16x64(wv[tn], av[tm], acc[tn][tm]);
+        } else if constexpr (AB == 32) {
+            const v4i zero = {0, 0, 0, 0};
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm) {
+                    fold4(accf[tn][tm], mfma16x16x64(wv[tn], half_operand(av[tm], kq, 0), zero),
+                          scur[tm][2 * h]);
+                    fold4(accf[tn][tm], mfma16x16x64(wv[tn], half_operand(av[tm], kq, 1), zero),
+                          scur[tm][2 * h + 1]);
+                }
+        } else if constexpr (AB == 64) {
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm)
+                    fold4(accf[tn][tm], mfma16x16x64(wv[tn], av[tm], v4i{0, 0, 0, 0}),
+                          scur[tm][h]);
+        } else {
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm) {
+                    acc[tn][tm] = mfma16x16x64(wv[tn], av[tm], acc[tn][tm]);
+                    if (h == 1) {
+                        fold4(accf[tn][tm], acc[tn][tm], scur[tm][0]);
+                        acc[tn][tm] = v4i{0, 0, 0, 0};
+                    }
+                }
+        }
     };
 
     // Workgroup barrier for the LDS stages: wait until this wavefront's LDS
@@ -538,15 +709,24 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
         rebuild_w(stage0);
         issue_act(0, stage0);
         if (nchunks > 1) fetch_w(1);
+        if constexpr (AB > 0) fetch_s(0, scur);
     }
     W4A8_LDS_BARRIER();
     auto iteration = [&](int64_t j, auto cur, auto nxt) {
         if (j + 1 < nchunks) rebuild_w(nxt);
         if (j + 2 < nchunks) fetch_w(j + 2);
         if (j + 1 < nchunks) issue_act(j + 1, nxt);
+        if constexpr (AB > 0)
+            if (j + 1 < nchunks) fetch_s(j + 1, snxt);
         mma_step(cur, 0);
         if ((j + 1) * kChunkK <= k) mma_step(cur, 1);
         W4A8_LDS_BARRIER();
+        if constexpr (AB > 0) {
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int b = 0; b < NBC; ++b) scur[tm][b] = snxt[tm][b];
+        }
     };
     for (int64_t j = 0; j < nchunks; j += 2) {
         iteration(j, stage0, stage1);
@@ -581,7 +761,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
                 const int r = tm * 16 + c - pass * rows_pass;
                 if (r < 0 || r >= rows_pass) continue;
                 const int64_t row = m0 + wm * WM + tm * 16 + c;
-                const float sa = a_scale[row < m ? row : m - 1];
+                const float sa = AB ? 1.0f : a_scale[row < m ? row : m - 1];
 #pragma unroll
                 for (int tn = 0; tn < TN; ++tn) {
                     const int col = tn * 16 + 4 * kq;             // within the wavefront tile
@@ -589,15 +769,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
                     const int byte = col * esize;
                     uint8_t *dst = ebuf + seg_off(r, byte >> 4) + (byte & 15);
                     const v4i a4 = acc[tn][tm];
-                    if (out_dtype == 2) {
+                    if (!AB && out_dtype == 2) {
                         *(v4i *)dst = a4;
                     } else {
                         const f32x4 sc = *(const f32x4 *)(ch_scale + (nn < n ? nn : n - 4));
                         float y[4];
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            y[i] = (float)a4[i] * sa;
-                            y[i] = y[i] * sc[i];
+                            if constexpr (AB > 0) {
+                                y[i] = accf[tn][tm][i] * sc[i];
+                            } else {
+                                y[i] = (float)a4[i] * sa;
+                                y[i] = y[i] * sc[i];
+                            }
                         }
                         if (out_dtype == 1)
                             *(u32x2 *)dst = u32x2{f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16),
@@ -626,7 +810,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
     }
 }
 
-template <int WF, int MT, int NT, bool FUSED, int AV = 1>
+template <int WF, int MT, int NT, bool FUSED, int AV = 1, int AB = 0>
 void launch_skinny(const void *act, const float *a_scale, const uint8_t *w_packed,
                    const uint8_t *grp_scale, const float *ch_scale, int64_t m, int64_t n,
                    int64_t k, void *out, int out_dtype, int8_t *ws_q, float *ws_s,
@@ -635,17 +819,18 @@ void launch_skinny(const void *act, const float *a_scale, const uint8_t *w_packe
     constexpr int WAVES = 8, D = FUSED ? 4 : (MT == 1 ? 4 : (MT == 2 ? 2 : 1));
     const int64_t ntiles = n / kNTile;
     const unsigned grid = (unsigned)((ntiles + NT - 1) / NT);
-    gemm_skinny_kernel<WF, MT, NT, WAVES, D, FUSED, AV><<<grid, 64 * WAVES, dyn_lds, stream>>>(
+    gemm_skinny_kernel<WF, MT, NT, WAVES, D, FUSED, AV, AB><<<grid, 64 * WAVES, dyn_lds,
+                                                            stream>>>(
         act, a_scale, w_packed, grp_scale, ch_scale, (int)m, n, k, out, out_dtype, ws_q, ws_s);
 }
 
-template <int WF, int BM, int BN, int WAVES_M, int WAVES_N>
+template <int WF, int BM, int BN, int WAVES_M, int WAVES_N, int AB = 0>
 void launch_tiled(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
                   const uint8_t *grp_scale, const float *ch_scale, int64_t m, int64_t n,
                   int64_t k, void *out, int out_dtype, hipStream_t stream) {
     const int64_t grid = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-    gemm_tiled_kernel<WF, BM, BN, WAVES_M, WAVES_N><<<(unsigned)grid, 64 * WAVES_M * WAVES_N,
-                                                      0, stream>>>(
+    gemm_tiled_kernel<WF, BM, BN, WAVES_M, WAVES_N, AB><<<(unsigned)grid,
+                                                          64 * WAVES_M * WAVES_N, 0, stream>>>(
         a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out, out_dtype);
 }
 
@@ -655,7 +840,7 @@ constexpr int64_t kFusedLdsMax = 48 * 1024;
 
 // Activation vectors per thread the fused prologue needs for m rows of k
 // (0 if the fused form does not apply).
-int fused_vectors(int64_t m, int64_t k) {
+[[maybe_unused]] int fused_vectors(int64_t m, int64_t k) {
     if (m < 1 || m > 16 || k <= 0) return 0;
     if (m * (k + 16) > kFusedLdsMax) return 0;
     int64_t tpr = 512;
@@ -721,6 +906,29 @@ hipError_t launch_gemm_bf16act_fmt(const uint16_t *a, const uint8_t *w_packed,
     if (e != hipSuccess) return e;
     return launch_gemm_fmt<WF>(ws_q, ws_s, w_packed, grp_scale, ch_scale, m, n, k, out,
                                out_dtype, stream);
+}
+
+// GEMM with per-block activation scales (AB = 32, 64 or 128) on int8
+// activations; output binary32 or bf16.
+template <int WF, int AB>
+hipError_t launch_gemm_blockact_fmt(const int8_t *a_q, const float *a_scale,
+                                    const uint8_t *w_packed, const uint8_t *grp_scale,
+                                    const float *ch_scale, int64_t m, int64_t n, int64_t k,
+                                    void *out, int out_dtype, hipStream_t stream) {
+    if (m == 0 || n == 0) return hipSuccess;
+    if (m <= 16)
+        launch_skinny<WF, 1, 1, false, 1, AB>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n,
+                                              k, out, out_dtype, nullptr, nullptr, 0, stream);
+    else if (m <= 32)
+        launch_skinny<WF, 2, 1, false, 1, AB>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n,
+                                              k, out, out_dtype, nullptr, nullptr, 0, stream);
+    else if (m <= 64)
+        launch_skinny<WF, 4, 1, false, 1, AB>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n,
+                                              k, out, out_dtype, nullptr, nullptr, 0, stream);
+    else
+        launch_tiled<WF, 128, 128, 2, 2, AB>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n,
+                                             k, out, out_dtype, stream);
+    return hipGetLastError();
 }
 
 }  // namespace

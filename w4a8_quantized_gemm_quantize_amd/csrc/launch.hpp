@@ -56,6 +56,14 @@ hipError_t launch_w8a8_gemm_bf16act(const uint16_t *a, const int8_t *w_packed,
                                     void *out, int out_dtype, int8_t *ws_q, float *ws_s,
                                     hipStream_t stream);
 
+// W4A8 GEMM with per-block activation scales a_scale[m][k / block], block in
+// {32, 64, 128}; out_dtype 0 (binary32) or 1 (bf16).
+hipError_t launch_w4a8_gemm_blockact(const int8_t *a_q, const float *a_scale,
+                                     const uint8_t *w_packed, const uint8_t *grp_scale,
+                                     const float *ch_scale, int64_t m, int64_t n, int64_t k,
+                                     int32_t block, void *out, int out_dtype,
+                                     hipStream_t stream);
+
 // EQuARX receive step: requantize(dequantize(q_in, s_in) + x) per block.
 hipError_t launch_dequant_add_requant(const int8_t *q_in, const float *s_in, const void *x,
                                       bool x_bf16, int64_t rows, int64_t cols, int32_t block,
