@@ -15,8 +15,11 @@ packed weights and activations (R copies total > 512 MB).
 Printed: one JSON line with the step throughput (TOPS = 2*M*N*K / step time),
 the dominant kernel's roofline (algorithmic bytes per launch / average launch
 time from HIP events on the launch stream), the standalone quantizer workload
-(64M bf16 elements, block 32 and 128: GB/s), and the CPU oracle timed on the
-host cores on a bounded sample (cpu_baseline).
+(64M bf16 elements, block 32 and 128: GB/s, dequantization round trip and its
+MSE), the extension paths (LQQ weights, W8A8 against W4A8 on a memory-bound and
+a compute-bound shape, per-block activation scales in the GEMM, the EQuARX
+dequantize-add-requantize step), and the CPU oracle timed on the host cores on
+a bounded sample (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -48,6 +51,7 @@ def parse():
                             "tiny"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-quantizer", action="store_true")
+    p.add_argument("--no-extensions", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 256 MiB device-to-device copy (reference for the "
@@ -67,6 +71,40 @@ def gemm_algorithmic_bytes(m, n, k, out_bytes, fused):
 def quantizer_algorithmic_bytes(elems, block):
     """bf16 in (2 B), int8 out (1 B), one fp32 scale per block."""
     return elems * 3 + 4 * (elems // block)
+
+
+def time_graph(torch, fn, copies, reps):
+    """Capture fn(r, stream) for r in range(copies) into one HIP graph, replay it
+    once untimed, then `reps` times between HIP events on the capture stream.
+    Returns the average milliseconds per fn call."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for r in range(copies):
+            fn(r, side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        s = torch.cuda.current_stream()
+        for r in range(copies):
+            fn(r, s)
+    stream = torch.cuda.current_stream()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * copies)
+
+
+def n_copies(per_copy_bytes):
+    """Distinct buffer sets needed for > 512 MB in rotation (cold MALL and L2)."""
+    return max(2, min(64, (512 << 20) // max(per_copy_bytes, 1) + 1))
 
 
 def profile_traffic(kernel_key: str, workload: str):
@@ -249,6 +287,8 @@ def main():
 
     if not args.no_quantizer:
         line["quantizer"] = quantizer_leg(torch, w4a8, inputs, dev, stream)
+    if not args.no_extensions:
+        line["extensions"] = extensions_leg(torch, w4a8, inputs, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(a_bits, w_bits, spec, args.cpu_seconds)
     print(json.dumps(line), flush=True)
@@ -259,11 +299,10 @@ def quantizer_leg(torch, w4a8, inputs, dev, stream, reps=20):
     and 128.  Two input/output sets alternate (2 x 200 MB) so reads come from HBM."""
     spec = inputs.QUANTIZER
     rows, cols = spec["rows"], spec["cols"]
-    g = torch.Generator(device=dev)
-    g.manual_seed(0)
-    xs = [torch.randn((rows, cols), generator=g, device=dev, dtype=torch.float32)
-          .to(torch.bfloat16) for _ in range(2)]
-    res = {"workload": f"{rows}x{cols} bf16 ~ N(0,1) (64M elements)"}
+    x0 = torch.from_numpy(inputs.activations(rows, cols, seed=0).view(np.int16)) \
+        .view(torch.bfloat16).to(dev)
+    xs = [x0, x0.clone()]
+    res = {"workload": f"{rows}x{cols} bf16 ~ N(0,1) (64M elements, seed 0)"}
     for block in spec["blocks"]:
         qs = [torch.empty((rows, cols), dtype=torch.int8, device=dev) for _ in range(2)]
         ss = [torch.empty((rows, cols // block), dtype=torch.float32, device=dev)
@@ -283,8 +322,131 @@ def quantizer_leg(torch, w4a8, inputs, dev, stream, reps=20):
         torch.cuda.synchronize()
         ms = float(np.mean([a.elapsed_time(b) for a, b in times]))
         gbps = quantizer_algorithmic_bytes(rows * cols, block) / (ms * 1e-3) / 1e9
-        res[f"block{block}"] = {"kernel_ms": ms, "achieved": gbps, "unit": "GB/s",
-                                "frac": gbps / HBM_PEAK_GBPS}
+        entry = {"kernel_ms": ms, "achieved": gbps, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS}
+        # dequantization round trip: q, scales -> fp32 and bf16; MSE against x
+        elems = rows * cols
+        for name, dt, ob in (("dequant_f32", torch.float32, 4), ("dequant_bf16", torch.bfloat16, 2)):
+            outs = [torch.empty((rows, cols), dtype=dt, device=dev) for _ in range(2)]
+
+            def deq(r, st, outs=outs, dt=dt):
+                w4a8.dequantize_act_blockwise(qs[r], ss[r], block, dt, out=outs[r], stream=st)
+            dms = time_graph(torch, deq, 2, 10)
+            dbytes = elems * (1 + ob) + 4 * (elems // block)
+            x64 = xs[0].double()
+            mse = float(((outs[0].double() - x64) ** 2).mean())
+            entry[name] = {"kernel_ms": dms, "achieved": dbytes / (dms * 1e-3) / 1e9,
+                           "unit": "GB/s", "mse": mse}
+        res[f"block{block}"] = entry
+    return res
+
+
+def extensions_leg(torch, w4a8, inputs, dev):
+    """The extension paths, each timed from a HIP graph over rotating buffer sets:
+    LQQ weights (decode shape, fused step), W8A8 against W4A8 (decode: memory-bound;
+    prefill: compute-bound, int8 activations), the GEMM with per-block activation
+    scales (decode shape, blocks 32 and 128; prefill shape, block 128) and the
+    EQuARX receive step (64M elements, bf16 partial sums, blocks 32 and 128)."""
+    res = {}
+
+    def bf16_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---- decode shape: LQQ, W8A8 and per-block scales
+    a_bits, w_bits, spec = inputs.workload_inputs("decode", seed=0)
+    m, n, k = spec["m"], spec["n"], spec["k"]
+    a = bf16_dev(a_bits)
+    w = bf16_dev(w_bits)
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(w4a8.workspace_bytes(m, k), dtype=torch.uint8, device=dev)
+    act_bytes = 2 * m * k + m * n * 2 + 4 * n
+
+    wp, gp, cs = w4a8.pack_w4_lqq(w)
+    c = n_copies(wp.numel() + 2 * gp.numel())
+    sets = [(wp, gp, cs)] + [(wp.clone(), gp.clone(), cs.clone()) for _ in range(c - 1)]
+    ms = time_graph(torch, lambda r, st: w4a8.w4a8_gemm_lqq_bf16act(
+        a, *sets[r], n, out=out, workspace=ws, stream=st), c, 4)
+    byt = n * k // 2 + 2 * n * (k // 64) + act_bytes
+    res["lqq_decode"] = {"shape": [m, n, k], "kernel_ms": ms, "achieved": byt / (ms * 1e-3) / 1e9,
+                         "unit": "GB/s", "frac": byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    del sets
+
+    w4p, g4, c4 = w4a8.pack_w4_grouped(w)
+    c = n_copies(w4p.numel() + g4.numel())
+    sets4 = [(w4p, g4, c4)] + [(w4p.clone(), g4.clone(), c4.clone()) for _ in range(c - 1)]
+    ms4 = time_graph(torch, lambda r, st: w4a8.w4a8_gemm_bf16act(
+        a, *sets4[r], n, out=out, workspace=ws, stream=st), c, 4)
+    w8p, c8 = w4a8.pack_w8_channel(w)
+    c = n_copies(w8p.numel())
+    sets8 = [(w8p, c8)] + [(w8p.clone(), c8.clone()) for _ in range(c - 1)]
+    ms8 = time_graph(torch, lambda r, st: w4a8.w8a8_gemm_bf16act(
+        a, *sets8[r], n, out=out, workspace=ws, stream=st), c, 4)
+    res["w8a8_vs_w4a8_decode"] = {
+        "shape": [m, n, k], "w4a8_ms": ms4, "w8a8_ms": ms8, "w4a8_speedup": ms8 / ms4,
+        "w8a8_achieved": (n * k + act_bytes) / (ms8 * 1e-3) / 1e9, "unit": "GB/s"}
+    del sets8
+
+    for block in (32, 128):
+        a_q, a_s = w4a8.quantize_act_blockwise(a, block)
+        ms = time_graph(torch, lambda r, st: w4a8.w4a8_gemm_blockact(
+            a_q, a_s, *sets4[r], n, block, out=out, stream=st), len(sets4), 4)
+        byt = n * k // 2 + n * (k // 64) + 4 * n + m * k + 4 * m * (k // block) + m * n * 2
+        res[f"blockact{block}_decode"] = {"shape": [m, n, k], "kernel_ms": ms,
+                                          "achieved": byt / (ms * 1e-3) / 1e9, "unit": "GB/s",
+                                          "frac": byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                          "per_token_ms": ms4}
+    del sets4
+
+    # ---- prefill shape: W8A8 vs W4A8 (compute-bound) and per-block scales
+    a_bits, w_bits, spec = inputs.workload_inputs("prefill", seed=0)
+    m, n, k = spec["m"], spec["n"], spec["k"]
+    a = bf16_dev(a_bits)
+    w = bf16_dev(w_bits)
+    a_q, a_s = w4a8.quantize_act_blockwise(a, k)
+    a_s = a_s.reshape(-1)
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    ops = 2.0 * m * n * k
+    w4p, g4, c4 = w4a8.pack_w4_grouped(w)
+    c = n_copies(w4p.numel() + m * k)
+    sets4 = [(w4p, g4, c4)] + [(w4p.clone(), g4.clone(), c4.clone()) for _ in range(c - 1)]
+    ms4 = time_graph(torch, lambda r, st: w4a8.w4a8_gemm(
+        a_q, a_s, *sets4[r], n, out=out, stream=st), c, 2)
+    w8p, c8 = w4a8.pack_w8_channel(w)
+    c8n = n_copies(w8p.numel() + m * k)
+    sets8 = [(w8p, c8)] + [(w8p.clone(), c8.clone()) for _ in range(c8n - 1)]
+    ms8 = time_graph(torch, lambda r, st: w4a8.w8a8_gemm(
+        a_q, a_s, *sets8[r], n, out=out, stream=st), c8n, 2)
+    del sets8
+    res["w8a8_vs_w4a8_prefill"] = {
+        "shape": [m, n, k], "w4a8_ms": ms4, "w8a8_ms": ms8, "w4a8_speedup": ms8 / ms4,
+        "w4a8_achieved": ops / (ms4 * 1e-3) / 1e12, "w8a8_achieved": ops / (ms8 * 1e-3) / 1e12,
+        "unit": "TFLOP/s", "peak": INT8_PEAK_TOPS}
+    a_qb, a_sb = w4a8.quantize_act_blockwise(a, 128)
+    ms = time_graph(torch, lambda r, st: w4a8.w4a8_gemm_blockact(
+        a_qb, a_sb, *sets4[r], n, 128, out=out, stream=st), c, 2)
+    res["blockact128_prefill"] = {"shape": [m, n, k], "kernel_ms": ms,
+                                  "achieved": ops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+                                  "frac": ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+                                  "per_token_ms": ms4}
+    del sets4, a, w
+
+    # ---- EQuARX receive step on the quantizer's 64M elements
+    qspec = inputs.QUANTIZER
+    rows, cols = qspec["rows"], qspec["cols"]
+    xs = [bf16_dev(inputs.activations(rows, cols, seed=s)) for s in (1, 2)]
+    for block in (32, 128):
+        qi, si = w4a8.quantize_act_blockwise(bf16_dev(inputs.activations(rows, cols, seed=3)),
+                                             block)
+        qo = [torch.empty_like(qi) for _ in range(2)]
+        so = [torch.empty_like(si) for _ in range(2)]
+        qis = [qi, qi.clone()]
+        sis = [si, si.clone()]
+        ms = time_graph(torch, lambda r, st: w4a8.dequant_add_requant(
+            qis[r], sis[r], xs[r], block, q_out=qo[r], s_out=so[r], stream=st), 2, 10)
+        elems = rows * cols
+        byt = elems * (1 + 2 + 1) + 2 * 4 * (elems // block)
+        res[f"equarx_step_block{block}"] = {
+            "elements": elems, "kernel_ms": ms, "achieved": byt / (ms * 1e-3) / 1e9,
+            "unit": "GB/s", "frac": byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
     return res
 
 
