@@ -50,6 +50,18 @@
 namespace w4a8 {
 namespace {
 
+// Workgroup barrier that waits only for this wavefront's LDS operations
+// (lgkmcnt(0)): global loads stay in flight across it, so weight batches
+// requested before it keep streaming in.  (__syncthreads() would wait for every
+// outstanding load.)  The empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Epilogue for channels n..n+3 of output row `row` (n % 4 == 0).
 __device__ __forceinline__ void store4(void *out, int out_dtype, int64_t row, int64_t ldo,
                                        int64_t n, v4i acc, float sa, f32x4 sc) {
@@ -154,7 +166,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 
     // Full 128-wide chunks are split evenly over the wavefronts; a trailing
     // 64-wide chunk (k % 128 == 64) is done by the last wavefront afterwards, so
-    // the batched loads below carry no data-dependent branches.
+    // the batched loads below carry no data-dependent branches.  The launchers
+    // only use this kernel for k >= 128 (at least one full chunk), so a
+    // wavefront without chunks of its own (j0 >= j1) still loads a valid one,
+    // chunk j1 - 1 = nfull - 1, and never uses it.
     const int64_t nfull = k / kChunkK;
     const bool has_half = nfull < nchunks;
     const int64_t per = (nfull + WAVES - 1) / WAVES;
@@ -203,8 +218,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 
     WeightBatch<WF, NT, D, MT, !FUSED, AB> cur;
     if constexpr (!FUSED) {
-        if (j0 < j1) load_batch(cur, j0);
-        __syncthreads();  // red cleared
+        load_batch(cur, j0);
+        lds_barrier();  // red cleared
     } else {
         // Per-row absmax -> scale, then the row's codes into LDS.  Threads are
         // split into m groups of tpr (a power of two) threads per row.  All
@@ -227,8 +242,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
         // The first weight batch is requested after the activations: loads
         // complete in order, so waiting for the activations below does not wait
         // for the weights, which stream in while the prologue runs.
-        if (j0 < j1) load_batch(cur, j0);
-        __syncthreads();  // red / amax_lds cleared
+        load_batch(cur, j0);
+        lds_barrier();  // red / amax_lds cleared
         float amax = 0.0f;
 #pragma unroll
         for (int u = 0; u < AV; ++u) {
@@ -258,7 +273,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
                     amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
                 if (row_ok && sub == 0) atomicMax(&amax_lds[row], __float_as_uint(amax));
             }
-            __syncthreads();
+            lds_barrier();
             float s;
             act_scale_pair(__uint_as_float(amax_lds[row_ok ? row : 0]), s, inv);
             if (row_ok && sub == 0) {
@@ -279,7 +294,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     v4i acc[NT][MT];
@@ -341,32 +356,46 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
         }
     };
 
-    for (int64_t jb = j0; jb < j1; jb += D) {
-        WeightBatch<WF, NT, D, MT, !FUSED, AB> nxt;
-        if (jb + D < j1) load_batch(nxt, jb + D);
+    // The chunks of batch b starting at jb (the first `cnt` of its D are used).
+    auto compute_batch = [&](const WeightBatch<WF, NT, D, MT, !FUSED, AB> &b, int64_t jb,
+                             int64_t cnt) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
+            if (d >= cnt) break;
             const int64_t j = jb + d;
-            if (j >= j1) break;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 uint32_t sv[NT];
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) sv[nt] = cur.s[d][nt][h];
+                for (int nt = 0; nt < NT; ++nt) sv[nt] = b.s[d][nt][h];
                 v4i av[MT];
                 if constexpr (FUSED) {
                     lds_act(av, j * kChunkK + h * kGroup + kq * 16);
                 } else {
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) av[mt] = cur.a[d][h][mt];
+                    for (int mt = 0; mt < MT; ++mt) av[mt] = b.a[d][h][mt];
                 }
                 mask_rows(av);
-                if constexpr (AB > 0) mma_step(cur.w[d], h, sv, av, cur.sa[d][h]);
-                else mma_step(cur.w[d], h, sv, av, sa_none);
+                if constexpr (AB > 0) mma_step(b.w[d], h, sv, av, b.sa[d][h]);
+                else mma_step(b.w[d], h, sv, av, sa_none);
             }
         }
+    };
+    // Software pipeline over batches: the next batch is requested before the
+    // current one is used.  The request sits in the loop body with no branch
+    // around it (a conditional load would make the compiler's wait at the join
+    // cover the prefetched batch too), and the last batch is peeled.
+    int64_t jb = j0;
+    for (; jb + D < j1; jb += D) {
+        WeightBatch<WF, NT, D, MT, !FUSED, AB> nxt;
+        load_batch(nxt, jb + D);
+        // keep the requests here: the scheduler would otherwise sink them below
+        // the uses of `cur` to reuse its registers, exposing their latency
+        __builtin_amdgcn_sched_barrier(0);
+        compute_batch(cur, jb, D);
         cur = nxt;
     }
+    if (jb < j1) compute_batch(cur, jb, j1 - jb);
 
     if (has_half && wave == WAVES - 1) {
         // Trailing 64-wide chunk: one K step.
@@ -816,7 +845,8 @@ void launch_skinny(const void *act, const float *a_scale, const uint8_t *w_packe
                    int64_t k, void *out, int out_dtype, int8_t *ws_q, float *ws_s,
                    size_t dyn_lds, hipStream_t stream) {
     // chunks per load batch: fewer when each batch also carries MT activation tiles
-    constexpr int WAVES = 8, D = FUSED ? 4 : (MT == 1 ? 4 : (MT == 2 ? 2 : 1));
+    constexpr int WAVES = 8,
+                  D = FUSED ? 4 : (MT == 1 ? 4 : (MT == 2 ? 2 : (NT == 1 && AB == 0 ? 2 : 1)));
     const int64_t ntiles = n / kNTile;
     const unsigned grid = (unsigned)((ntiles + NT - 1) / NT);
     gemm_skinny_kernel<WF, MT, NT, WAVES, D, FUSED, AV, AB><<<grid, 64 * WAVES, dyn_lds,
@@ -841,7 +871,7 @@ constexpr int64_t kFusedLdsMax = 48 * 1024;
 // Activation vectors per thread the fused prologue needs for m rows of k
 // (0 if the fused form does not apply).
 [[maybe_unused]] int fused_vectors(int64_t m, int64_t k) {
-    if (m < 1 || m > 16 || k <= 0) return 0;
+    if (m < 1 || m > 16 || k < kChunkK) return 0;
     if (m * (k + 16) > kFusedLdsMax) return 0;
     int64_t tpr = 512;
     while (tpr * m > 512) tpr >>= 1;
@@ -857,7 +887,11 @@ hipError_t launch_gemm_fmt(const int8_t *a_q, const float *a_scale, const uint8_
                             hipStream_t stream) {
     if (m == 0 || n == 0) return hipSuccess;
     const int64_t ntiles = n / kNTile;
-    if (m <= 16) {
+    if (k < kChunkK) {
+        // no full 128-wide chunk: the skinny kernel's loads assume one
+        launch_tiled<WF, 128, 128, 2, 2>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k,
+                                         out, out_dtype, stream);
+    } else if (m <= 16) {
         launch_skinny<WF, 1, 1, false>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out,
                                    out_dtype, nullptr, nullptr, 0, stream);
     } else if (m <= 32) {
@@ -916,7 +950,10 @@ hipError_t launch_gemm_blockact_fmt(const int8_t *a_q, const float *a_scale,
                                     const float *ch_scale, int64_t m, int64_t n, int64_t k,
                                     void *out, int out_dtype, hipStream_t stream) {
     if (m == 0 || n == 0) return hipSuccess;
-    if (m <= 16)
+    if (k < kChunkK)
+        launch_tiled<WF, 128, 128, 2, 2, AB>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n,
+                                             k, out, out_dtype, stream);
+    else if (m <= 16)
         launch_skinny<WF, 1, 1, false, 1, AB>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n,
                                               k, out, out_dtype, nullptr, nullptr, 0, stream);
     else if (m <= 32)
