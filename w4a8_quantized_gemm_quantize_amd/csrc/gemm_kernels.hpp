@@ -587,11 +587,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
     // after the load; its missing second group reuses the first group's
     // parameter.  An int8 half chunk holds step 0 only, whose address is
     // reloaded in place of step 1.
-    WRec<WF> wrec[TPW];
-    uint32_t wsc[TPW][2];
-    bool wfull = true;
-    auto fetch_w = [&](int64_t j) {
-        wfull = (j + 1) * kChunkK <= k;
+    //
+    // Two register sets, by parity of the chunk index: the records of chunk
+    // j + 3 are requested while chunk j is multiplied, so each set has two
+    // iterations to arrive before its rebuild.  Requests past the last chunk
+    // are clamped to it (fetched, never used), so no branch surrounds them.
+    WRec<WF> wrec0[TPW], wrec1[TPW];
+    uint32_t wsc0[TPW][2], wsc1[TPW][2];
+    constexpr int kWLoads = (WF == kW8 ? 2 : 3) * TPW;   // loads per fetch_w
+    auto fetch_w = [&](int64_t jreq, auto set_tag) {
+        WRec<WF>(&wrec)[TPW] = decltype(set_tag)::value ? wrec1 : wrec0;
+        uint32_t(&wsc)[TPW][2] = decltype(set_tag)::value ? wsc1 : wsc0;
+        const int64_t j = jreq < nchunks ? jreq : nchunks - 1;
+        const bool wfull = (j + 1) * kChunkK <= k;
         const int64_t g1 = wfull ? 2 * j + 1 : 2 * j;
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
@@ -609,9 +617,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
             }
         }
     };
-    // Rebuild the int8 operands of both K steps into stage buf.
-    auto rebuild_w = [&](auto buf_tag) {
+    // Rebuild the int8 operands of both K steps of chunk j (from the register
+    // set of its parity) into the LDS stage of the same parity.
+    auto rebuild_w = [&](int64_t j, auto buf_tag) {
         uint8_t *wbase = decltype(buf_tag)::value ? wl1 : wl0;
+        WRec<WF>(&wrec)[TPW] = decltype(buf_tag)::value ? wrec1 : wrec0;
+        uint32_t(&wsc)[TPW][2] = decltype(buf_tag)::value ? wsc1 : wsc0;
+        const bool wfull = (j + 1) * kChunkK <= k;
         if constexpr (WF != kW8) {
             if (!wfull) {
 #pragma unroll
@@ -724,32 +736,47 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
     } while (0)
 
     // Pipeline over K chunks: iteration j multiplies stage `cur` while stage
-    // `nxt` is filled for chunk j + 1.  Its first act is rebuilding this
-    // wavefront's weight tile(s) of chunk j + 1 into `nxt` from records
-    // fetched during iteration j - 1; then it fetches the records of chunk
-    // j + 2 and issues the direct-to-LDS activation loads of chunk j + 1, so
-    // both kinds of load have a whole iteration of MFMAs to arrive.  (The LDS
-    // writes come before the direct loads because the compiler makes any LDS
-    // store wait for direct-to-LDS loads still in flight.)
+    // `nxt` is filled for chunk j + 1.  It issues the direct-to-LDS activation
+    // loads of chunk j + 1, runs the first K step of chunk j, rebuilds this
+    // wavefront's weight tile(s) of chunk j + 1 into `nxt` (records fetched
+    // two iterations earlier) while those MFMAs run, requests the records of
+    // chunk j + 3 into the register set just consumed, and runs the second K
+    // step.  The scheduling barriers keep that order, on which the barrier's
+    // wait count relies.
+    // The barrier at the end waits for everything but the last kWLoads
+    // requests (vmcnt completes in order): the activations of chunk j + 1 and
+    // the records of chunk j + 2 are in, the records of chunk j + 3 stay in
+    // flight.  (The LDS writes of the rebuild come first because the compiler
+    // makes any LDS store wait for direct-to-LDS loads still in flight.)
     const std::integral_constant<bool, false> stage0;
     const std::integral_constant<bool, true> stage1;
     if (nchunks > 0) {
-        fetch_w(0);
-        rebuild_w(stage0);
+        fetch_w(0, stage0);
+        fetch_w(1, stage1);
+        rebuild_w(0, stage0);
+        fetch_w(2, stage0);
         issue_act(0, stage0);
-        if (nchunks > 1) fetch_w(1);
         if constexpr (AB > 0) fetch_s(0, scur);
     }
     W4A8_LDS_BARRIER();
+    // lgkmcnt(0) and vmcnt(kWLoads) (expcnt left at its maximum)
+    constexpr int kPartialWait = (kWLoads & 15) | ((kWLoads >> 4) << 14) | 0x70;
+    static_assert(kWLoads < 64, "vmcnt field");
     auto iteration = [&](int64_t j, auto cur, auto nxt) {
-        if (j + 1 < nchunks) rebuild_w(nxt);
-        if (j + 2 < nchunks) fetch_w(j + 2);
         if (j + 1 < nchunks) issue_act(j + 1, nxt);
         if constexpr (AB > 0)
             if (j + 1 < nchunks) fetch_s(j + 1, snxt);
         mma_step(cur, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j + 1 < nchunks) rebuild_w(j + 1, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch_w(j + 3, nxt);
+        __builtin_amdgcn_sched_barrier(0);
         if ((j + 1) * kChunkK <= k) mma_step(cur, 1);
-        W4A8_LDS_BARRIER();
+        __builtin_amdgcn_s_waitcnt(kPartialWait);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
         if constexpr (AB > 0) {
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm)
@@ -761,6 +788,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
         iteration(j, stage0, stage1);
         if (j + 1 < nchunks) iteration(j + 1, stage1, stage0);
     }
+    // the clamped requests past the last chunk: done before the stages are reused
+    W4A8_LDS_BARRIER();
 #undef W4A8_LDS_BARRIER
 
     // Epilogue through LDS (free after the last barrier): each wavefront writes
