@@ -119,7 +119,13 @@ __device__ __forceinline__ v4i half_operand(v4i a, int kq, int half) {
 }
 
 // ---------------------------------------------------------------- skinny --
-constexpr int kSkinnyMaxVec = 16;   // fused prologue: 16-byte vectors held per thread
+constexpr int kSkinnyMaxVec = 8;    // fused prologue: 16-byte vectors held per thread
+// Wavefronts per workgroup of the fused form: 16 when the weight stream per
+// workgroup is short (the quantization prologue, which every workgroup runs over
+// all of A, then dominates and gets four wavefronts per SIMD), else 8 with
+// deeper load batches for the long stream.
+constexpr int64_t kFusedShortK = 8192;
+inline int fused_waves(int64_t k) { return k <= kFusedShortK ? 16 : 8; }
 
 template <int WF, int NT, int D, int MT, bool WITH_ACT, int AB>
 struct WeightBatch {
@@ -868,14 +874,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
     }
 }
 
-template <int WF, int MT, int NT, bool FUSED, int AV = 1, int AB = 0>
+template <int WF, int MT, int NT, bool FUSED, int AV = 1, int AB = 0, int FW = 8>
 void launch_skinny(const void *act, const float *a_scale, const uint8_t *w_packed,
                    const uint8_t *grp_scale, const float *ch_scale, int64_t m, int64_t n,
                    int64_t k, void *out, int out_dtype, int8_t *ws_q, float *ws_s,
                    size_t dyn_lds, hipStream_t stream) {
-    // chunks per load batch: fewer when each batch also carries MT activation tiles
-    constexpr int WAVES = 8,
-                  D = FUSED ? 4 : (MT == 1 ? 4 : (MT == 2 ? 2 : (NT == 1 && AB == 0 ? 2 : 1)));
+    // chunks per load batch: fewer when each batch also carries MT activation
+    // tiles.  The fused form runs 16 wavefronts so its quantization prologue
+    // (every workgroup converts all of A) has four wavefronts per SIMD.
+    constexpr int WAVES = FUSED ? FW : 8,
+                  D = FUSED ? (FW == 16 ? 2 : 4)
+                            : (MT == 1 ? 4 : (MT == 2 ? 2 : (NT == 1 && AB == 0 ? 2 : 1)));
     const int64_t ntiles = n / kNTile;
     const unsigned grid = (unsigned)((ntiles + NT - 1) / NT);
     gemm_skinny_kernel<WF, MT, NT, WAVES, D, FUSED, AV, AB><<<grid, 64 * WAVES, dyn_lds,
@@ -902,10 +911,11 @@ constexpr int64_t kFusedLdsMax = 48 * 1024;
 [[maybe_unused]] int fused_vectors(int64_t m, int64_t k) {
     if (m < 1 || m > 16 || k < kChunkK) return 0;
     if (m * (k + 16) > kFusedLdsMax) return 0;
-    int64_t tpr = 512;
-    while (tpr * m > 512) tpr >>= 1;
+    const int64_t threads = 64 * fused_waves(k);
+    int64_t tpr = threads;
+    while (tpr * m > threads) tpr >>= 1;
     const int64_t need = (k / 8 + tpr - 1) / tpr;
-    return need <= 4 ? 4 : need <= 8 ? 8 : need <= kSkinnyMaxVec ? 16 : 0;
+    return need <= 4 ? 4 : need <= kSkinnyMaxVec ? 8 : 0;
 }
 
 // GEMM on int8 activations for weight format WF.
@@ -954,15 +964,21 @@ hipError_t launch_gemm_bf16act_fmt(const uint16_t *a, const uint8_t *w_packed,
     const int av = fused_vectors(m, k);
     if (av > 0) {
         const size_t lds_bytes = (size_t)(m * (k + 16));
-        if (av == 4)
-            launch_skinny<WF, 1, 1, true, 4>(a, nullptr, w_packed, grp_scale, ch_scale, m, n, k, out,
-                                         out_dtype, ws_q, ws_s, lds_bytes, stream);
-        else if (av == 8)
-            launch_skinny<WF, 1, 1, true, 8>(a, nullptr, w_packed, grp_scale, ch_scale, m, n, k, out,
-                                         out_dtype, ws_q, ws_s, lds_bytes, stream);
+        const bool w16 = fused_waves(k) == 16;
+        if (av == 4 && w16)
+            launch_skinny<WF, 1, 1, true, 4, 0, 16>(a, nullptr, w_packed, grp_scale, ch_scale, m,
+                                                    n, k, out, out_dtype, ws_q, ws_s, lds_bytes,
+                                                    stream);
+        else if (w16)
+            launch_skinny<WF, 1, 1, true, 8, 0, 16>(a, nullptr, w_packed, grp_scale, ch_scale, m,
+                                                    n, k, out, out_dtype, ws_q, ws_s, lds_bytes,
+                                                    stream);
+        else if (av == 4)
+            launch_skinny<WF, 1, 1, true, 4, 0, 8>(a, nullptr, w_packed, grp_scale, ch_scale, m, n,
+                                                   k, out, out_dtype, ws_q, ws_s, lds_bytes, stream);
         else
-            launch_skinny<WF, 1, 1, true, 16>(a, nullptr, w_packed, grp_scale, ch_scale, m, n, k,
-                                          out, out_dtype, ws_q, ws_s, lds_bytes, stream);
+            launch_skinny<WF, 1, 1, true, 8, 0, 8>(a, nullptr, w_packed, grp_scale, ch_scale, m, n,
+                                                   k, out, out_dtype, ws_q, ws_s, lds_bytes, stream);
         return hipGetLastError();
     }
     hipError_t e = launch_quantize_act(a, m, k, (int32_t)k, ws_q, ws_s, stream);
