@@ -317,3 +317,35 @@ def test_blockact_argument_errors(w4a8):
             w4a8.w4a8_gemm_blockact(a, s, wp, gs, cs, 16, block, out_dtype=torch.float32)
     with pytest.raises(w4a8.W4A8Error):
         w4a8.w4a8_gemm_blockact(a, s, wp, gs, cs, 16, 64, out_dtype=torch.int32)
+
+
+# ------------------------------------- large products split by tile size --
+
+@pytest.mark.parametrize("fmt", ["w4", "lqq", "w8"])
+def test_large_product_split_into_two_tile_sizes(w4a8, fmt):
+    """258 large tiles on 256 compute units: the launcher runs 256 of them as
+    256 x 256 tiles and the last column of tiles as 128 x 256 tiles (a second
+    launch on a column range).  Every output must still match the oracle."""
+    m, n, k = 512, 33024, 128
+    announce("split launch", fmt, m, n, k)
+    w = inputs.weights(n, k, seed=31)
+    a_q, a_s = oracle.quantize_act_blockwise(inputs.activations(m, k, seed=31), k)
+    aq_d, as_d = torch.from_numpy(a_q).cuda(), torch.from_numpy(a_s.reshape(-1)).cuda()
+    if fmt == "w4":
+        dev_w = w4a8.pack_w4_grouped(to_dev_bf16(w))
+        acc = w4a8.w4a8_gemm(aq_d, as_d, *dev_w, n, out_dtype=torch.int32)
+        y = w4a8.w4a8_gemm(aq_d, as_d, *dev_w, n, out_dtype=torch.bfloat16)
+        acc_ref, y_ref = oracle.w4a8_gemm(a_q, a_s, *oracle.quantize_w4_grouped(w, 64), 64)
+    elif fmt == "lqq":
+        dev_w = w4a8.pack_w4_lqq(to_dev_bf16(w))
+        acc = w4a8.w4a8_gemm_lqq(aq_d, as_d, *dev_w, n, out_dtype=torch.int32)
+        y = w4a8.w4a8_gemm_lqq(aq_d, as_d, *dev_w, n, out_dtype=torch.bfloat16)
+        acc_ref, y_ref = oracle.w4a8_gemm_lqq(a_q, a_s, *oracle.quantize_w4_lqq(w, 64), 64)
+    else:
+        dev_w = w4a8.pack_w8_channel(to_dev_bf16(w))
+        acc = w4a8.w8a8_gemm(aq_d, as_d, *dev_w, n, out_dtype=torch.int32)
+        y = w4a8.w8a8_gemm(aq_d, as_d, *dev_w, n, out_dtype=torch.bfloat16)
+        acc_ref, y_ref = oracle.w8a8_gemm(a_q, a_s, *oracle.quantize_w8_channel(w))
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    assert_bf16_within_ulp(bits_of(y), y_ref)

@@ -522,7 +522,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
     const int8_t *__restrict__ a_q, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ w_packed, const uint8_t *__restrict__ grp_scale,
     const float *__restrict__ ch_scale, int64_t m, int64_t n, int64_t k,
-    void *__restrict__ out, int out_dtype) {
+    void *__restrict__ out, int64_t ldo, int out_dtype) {
     using L = TiledLds<BM, BN>;
     constexpr int WAVES = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -867,7 +867,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
                 const int64_t nn = n0 + wn * WN + (seg * 16) / esize;
                 const u32x4 v = *(const u32x4 *)(ebuf + seg_off(r, seg));
                 if (row < m && nn < n)
-                    *(u32x4 *)((uint8_t *)out + (row * n + nn) * esize) = v;
+                    *(u32x4 *)((uint8_t *)out + (row * ldo + nn) * esize) = v;
             }
             asm volatile("" ::: "memory");
         }
@@ -892,14 +892,66 @@ void launch_skinny(const void *act, const float *a_scale, const uint8_t *w_packe
         act, a_scale, w_packed, grp_scale, ch_scale, (int)m, n, k, out, out_dtype, ws_q, ws_s);
 }
 
+// Output columns [n_off, n_off + n_sub) of an [m, ldo] product: the weight
+// pointers move by whole 16-channel tiles (tile-major layouts).
+template <int WF, int BM, int BN, int WAVES_M, int WAVES_N, int AB = 0>
+void launch_tiled_cols(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
+                       const uint8_t *grp_scale, const float *ch_scale, int64_t m, int64_t n_off,
+                       int64_t n_sub, int64_t ldo, int64_t k, void *out, int out_dtype,
+                       hipStream_t stream) {
+    if (n_sub <= 0) return;
+    const int64_t t_off = n_off / kNTile;
+    const int64_t wtile = WF == kW8 ? kNTile * k : kNTile * k / 2;      // bytes per tile
+    const int64_t ptile = kNTile * (k / kGroup) * (WF == kW4Lqq ? 2 : 1);  // parameter bytes
+    const int esize = out_dtype == 1 ? 2 : 4;
+    const int64_t grid = ((m + BM - 1) / BM) * ((n_sub + BN - 1) / BN);
+    gemm_tiled_kernel<WF, BM, BN, WAVES_M, WAVES_N, AB><<<(unsigned)grid,
+                                                          64 * WAVES_M * WAVES_N, 0, stream>>>(
+        a_q, a_scale, w_packed + t_off * wtile,
+        grp_scale ? grp_scale + t_off * ptile : grp_scale, ch_scale + n_off, m, n_sub, k,
+        (uint8_t *)out + n_off * esize, ldo, out_dtype);
+}
+
 template <int WF, int BM, int BN, int WAVES_M, int WAVES_N, int AB = 0>
 void launch_tiled(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
                   const uint8_t *grp_scale, const float *ch_scale, int64_t m, int64_t n,
                   int64_t k, void *out, int out_dtype, hipStream_t stream) {
-    const int64_t grid = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-    gemm_tiled_kernel<WF, BM, BN, WAVES_M, WAVES_N, AB><<<(unsigned)grid,
-                                                          64 * WAVES_M * WAVES_N, 0, stream>>>(
-        a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out, out_dtype);
+    launch_tiled_cols<WF, BM, BN, WAVES_M, WAVES_N, AB>(a_q, a_scale, w_packed, grp_scale,
+                                                        ch_scale, m, 0, n, n, k, out, out_dtype,
+                                                        stream);
+}
+
+// Large products: whole rounds of 256 x 256 tiles (one workgroup per compute
+// unit) over a leading range of output columns, and the remaining columns in
+// 128 x 256 tiles, half the work each, when that shortens the last round
+// (e.g. 896 tiles on 256 compute units: 3 rounds of large tiles + half a round
+// of small ones instead of 4 rounds).
+template <int WF>
+void launch_tiled_large(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
+                        const uint8_t *grp_scale, const float *ch_scale, int64_t m, int64_t n,
+                        int64_t k, void *out, int out_dtype, hipStream_t stream) {
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        ncu <= 0)
+        ncu = 256;
+    const int64_t mt = (m + 255) / 256, ntb = (n + 255) / 256;
+    auto rounds = [&](int64_t tiles) { return (tiles + ncu - 1) / ncu; };
+    // cost in units of one round of large tiles; large-tile columns first
+    int64_t best_cols = ntb;
+    double best = (double)rounds(mt * ntb);
+    for (int64_t cols = ntb - 1; cols >= 0; --cols) {
+        const double c = (double)rounds(mt * cols) + 0.5 * (double)rounds(2 * mt * (ntb - cols));
+        if (c < best - 1e-9) {
+            best = c;
+            best_cols = cols;
+        }
+    }
+    const int64_t n_large = best_cols * 256 < n ? best_cols * 256 : n;
+    launch_tiled_cols<WF, 256, 256, 4, 4>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, 0,
+                                          n_large, n, k, out, out_dtype, stream);
+    launch_tiled_cols<WF, 128, 256, 2, 4>(a_q, a_scale, w_packed, grp_scale, ch_scale, m,
+                                          n_large, n - n_large, n, k, out, out_dtype, stream);
 }
 
 // Largest m * (k + 16) the fused skinny prologue keeps in LDS, and the vectors
@@ -947,7 +999,7 @@ hipError_t launch_gemm_fmt(const int8_t *a_q, const float *a_scale, const uint8_
         launch_tiled<WF, 128, 128, 2, 2>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out,
                                out_dtype, stream);
     } else {
-        launch_tiled<WF, 256, 256, 4, 4>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out,
+        launch_tiled_large<WF>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out,
                                out_dtype, stream);
     }
     return hipGetLastError();
