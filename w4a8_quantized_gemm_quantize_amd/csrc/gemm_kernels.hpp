@@ -518,7 +518,7 @@ __device__ __forceinline__ int act_lds_off(int row, int c16) {
 // AB: 0 = per-token activation scales; 32, 64 or 128 = per-block scales
 // a_scale[m][k / AB], each block's int32 partial folded into binary32 in K order.
 template <int WF, int BM, int BN, int WAVES_M, int WAVES_N, int AB = 0>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_tiled_kernel(
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 : 1) void gemm_tiled_kernel(
     const int8_t *__restrict__ a_q, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ w_packed, const uint8_t *__restrict__ grp_scale,
     const float *__restrict__ ch_scale, int64_t m, int64_t n, int64_t k,
