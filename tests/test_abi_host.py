@@ -146,3 +146,76 @@ def test_bf16act_workspace_and_validation(lib):
     assert f(A, B, C, D, 8, 64, 4096, 64, E, 1, MIS, need, NUL) == ERR_MISALIGNED
     assert f(A, B, C, D, 8, 64, 0, 64, E, 1, A, need, NUL) == ERR_SHAPE    # k == 0
     assert f(A, B, C, D, 8, 64, 4096, 32, E, 1, A, need, NUL) == ERR_UNSUPPORTED
+
+
+@pytest.fixture(scope="module")
+def ext(lib):
+    P, I64, I32, INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+    lib.pack_w4_lqq.argtypes = [P, I64, I64, I32, P, P, P, P]
+    lib.unpack_w4_lqq.argtypes = [P, P, I64, I64, I32, P, P, P, P]
+    lib.w4a8_gemm_lqq.argtypes = [P, P, P, P, P, I64, I64, I64, I32, P, INT, P]
+    lib.w4a8_gemm_lqq_bf16act.argtypes = [P, P, P, P, I64, I64, I64, I32, P, INT, P,
+                                          ctypes.c_size_t, P]
+    lib.pack_w8_channel.argtypes = [P, I64, I64, P, P, P]
+    lib.unpack_w8_channel.argtypes = [P, I64, I64, P, P]
+    lib.w8a8_gemm.argtypes = [P, P, P, P, I64, I64, I64, P, INT, P]
+    lib.w8a8_gemm_bf16act.argtypes = [P, P, P, I64, I64, I64, P, INT, P, ctypes.c_size_t, P]
+    lib.w4a8_gemm_blockact.argtypes = [P, P, P, P, P, I64, I64, I64, I32, I32, P, INT, P]
+    lib.dequant_add_requant.argtypes = [P, P, P, INT, I64, I64, I32, P, P, P, P]
+    return lib
+
+
+def test_extension_entry_points_declared():
+    names = declared_functions()
+    for want in ["pack_w4_lqq", "unpack_w4_lqq", "w4a8_gemm_lqq", "w4a8_gemm_lqq_bf16act",
+                 "pack_w8_channel", "unpack_w8_channel", "w8a8_gemm", "w8a8_gemm_bf16act",
+                 "w4a8_gemm_blockact", "dequant_add_requant"]:
+        assert want in names
+
+
+def test_lqq_validation(ext):
+    lqq_kmax = 133120
+    assert lqq_kmax == (2**31 - 1) // (127 * 127) // 64 * 64
+    p = ext.pack_w4_lqq
+    assert p(A, 32, 256, 128, B, C, D, NUL) == ERR_UNSUPPORTED
+    assert p(A, 20, 256, 64, B, C, D, NUL) == ERR_SHAPE
+    assert p(A, 32, 256, 64, B, NUL, D, NUL) == ERR_NULL
+    assert p(A, 32, 256, 64, B, MIS, D, NUL) == ERR_MISALIGNED
+    u = ext.unpack_w4_lqq
+    assert u(A, B, 32, 256, 64, C, D, NUL, NUL) == ERR_NULL
+    g = ext.w4a8_gemm_lqq
+    # the W4 bound (150976) is too large for LQQ operands: the LQQ bound applies
+    assert g(A, B, C, D, E, 8, 64, lqq_kmax + 64, 64, A, 0, NUL) == ERR_UNSUPPORTED
+    assert g(A, B, C, NUL, E, 8, 64, 256, 64, A, 0, NUL) == ERR_NULL
+    f = ext.w4a8_gemm_lqq_bf16act
+    need = ext.w4a8_gemm_bf16act_workspace_bytes(8, 256)
+    assert f(A, B, C, D, 8, 64, 256, 64, E, 1, A, need - 1, NUL) == ERR_SHAPE
+    assert f(A, B, C, D, 8, 64, lqq_kmax + 64, 64, E, 1, A, 1 << 30, NUL) == ERR_UNSUPPORTED
+
+
+def test_w8a8_validation(ext):
+    assert ext.pack_w8_channel(A, 24, 256, B, C, NUL) == ERR_SHAPE
+    assert ext.pack_w8_channel(A, 32, 256, NUL, C, NUL) == ERR_NULL
+    assert ext.unpack_w8_channel(A, 32, 100, B, NUL) == ERR_SHAPE
+    g = ext.w8a8_gemm
+    assert g(A, B, C, D, 8, 64, 133120 + 64, E, 0, NUL) == ERR_UNSUPPORTED
+    assert g(A, B, NUL, D, 8, 64, 256, E, 0, NUL) == ERR_NULL
+    assert g(A, B, C, D, 8, 64, 256, MIS, 0, NUL) == ERR_MISALIGNED
+    assert g(NUL, NUL, NUL, NUL, 0, 64, 256, NUL, 1, NUL) == OK
+
+
+def test_blockact_validation(ext):
+    g = ext.w4a8_gemm_blockact
+    assert g(A, B, C, D, E, 8, 64, 256, 64, 48, A, 0, NUL) == ERR_UNSUPPORTED   # block 48
+    assert g(A, B, C, D, E, 8, 64, 256, 64, 256, A, 0, NUL) == ERR_UNSUPPORTED  # block 256
+    assert g(A, B, C, D, E, 8, 64, 192, 64, 128, A, 0, NUL) == ERR_SHAPE        # 192 % 128
+    assert g(A, B, C, D, E, 8, 64, 256, 64, 64, A, 2, NUL) == ERR_UNSUPPORTED   # int32 out
+    assert g(A, NUL, C, D, E, 8, 64, 256, 64, 64, A, 0, NUL) == ERR_NULL
+
+
+def test_dequant_add_requant_validation(ext):
+    f = ext.dequant_add_requant
+    assert f(A, B, C, 0, 4, 64, 48, D, E, A, NUL) == ERR_SHAPE       # 64 % 48
+    assert f(A, B, C, 2, 4, 64, 32, D, E, A, NUL) == ERR_UNSUPPORTED  # int32 partial sums
+    assert f(A, B, NUL, 0, 4, 64, 32, D, E, A, NUL) == ERR_NULL
+    assert f(A, B, C, 1, 4, 64, 32, MIS, E, A, NUL) == ERR_MISALIGNED  # sum_out misaligned

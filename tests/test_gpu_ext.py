@@ -349,3 +349,107 @@ def test_large_product_split_into_two_tile_sizes(w4a8, fmt):
     torch.cuda.synchronize()
     assert np.array_equal(acc.cpu().numpy(), acc_ref)
     assert_bf16_within_ulp(bits_of(y), y_ref)
+
+
+# ------------------------------------------------------- int32 headroom --
+
+def _const_weights(n, k, value=0.5):
+    return inputs.f32_to_bf16_bits(np.full((n, k), value, np.float32))
+
+
+@pytest.mark.parametrize("m", [2, 65])
+def test_w4_gemm_at_k_max_with_extreme_operands(w4a8, m):
+    """K = W4A8_K_MAX, every activation code 127, every rebuilt weight 112 (q = 7,
+    s_g = 16): acc = 127 * 112 * K = 2,147,462,144, just below 2^31.  Skinny
+    (m = 2) and tiled (m = 65) kernels both accumulate it exactly."""
+    k, n = w4a8.K_MAX, 16
+    announce("k_max w4", m, n, k)
+    w = _const_weights(n, k)
+    wp, gs, cs = w4a8.pack_w4_grouped(to_dev_bf16(w))
+    a_q = np.full((m, k), 127, np.int8)
+    a_s = np.ones(m, np.float32)
+    acc = w4a8.w4a8_gemm(torch.from_numpy(a_q).cuda(), torch.from_numpy(a_s).cuda(), wp, gs, cs,
+                         n, out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    acc_ref, _ = oracle.w4a8_gemm(a_q, a_s, *oracle.quantize_w4_grouped(w, 64), 64,
+                                  want_y=False)
+    assert int(acc_ref.max()) == 127 * 112 * k
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+
+
+def test_fused_at_k_max(w4a8):
+    m, n, k = 3, 32, w4a8.K_MAX
+    announce("k_max fused", m, n, k)
+    w = _const_weights(n, k, -0.25)
+    a = inputs.f32_to_bf16_bits(np.full((m, k), 3.0, np.float32))
+    wp, gs, cs = w4a8.pack_w4_grouped(to_dev_bf16(w))
+    acc = w4a8.w4a8_gemm_bf16act(to_dev_bf16(a), wp, gs, cs, n, out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    _, _, acc_ref, _ = oracle.w4a8_gemm_bf16act(a, *oracle.quantize_w4_grouped(w, 64), 64)
+    assert int(acc_ref.min()) == -127 * 112 * k
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+
+
+def test_w8a8_at_lqq_k_max(w4a8):
+    m, n, k = 2, 16, w4a8.LQQ_K_MAX
+    announce("k_max w8", m, n, k)
+    w = _const_weights(n, k)
+    wp, cs = w4a8.pack_w8_channel(to_dev_bf16(w))
+    a_q = np.full((m, k), -127, np.int8)
+    a_s = np.ones(m, np.float32)
+    acc = w4a8.w8a8_gemm(torch.from_numpy(a_q).cuda(), torch.from_numpy(a_s).cuda(), wp, cs, n,
+                         out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    acc_ref, _ = oracle.w8a8_gemm(a_q, a_s, *oracle.quantize_w8_channel(w), want_y=False)
+    assert int(acc_ref.min()) == -127 * 127 * k
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+
+
+# ------------------------------------------------------------ HIP graphs --
+
+def test_extension_calls_replay_in_a_graph(w4a8):
+    """LQQ, W8A8, per-block-scale and EQuARX-step calls captured in one HIP graph
+    replay to their eager results, with eager work and syncs between replays."""
+    m, n, k = 8, 256, 1024
+    announce("graph replay ext", m, n, k)
+    w = to_dev_bf16(inputs.weights(n, k, seed=41))
+    a = to_dev_bf16(inputs.activations(m, k, seed=41))
+    lqq = w4a8.pack_w4_lqq(w)
+    w8 = w4a8.pack_w8_channel(w)
+    w4 = w4a8.pack_w4_grouped(w)
+    qb, sb = w4a8.quantize_act_blockwise(a, 32)
+    x = to_dev_bf16(inputs.activations(m, k, seed=42))
+    ws = torch.empty(w4a8.workspace_bytes(m, k), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((m, n), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    q_o = torch.empty((m, k), dtype=torch.int8, device="cuda")
+    s_o = torch.empty((m, k // 32), dtype=torch.float32, device="cuda")
+
+    def run(stream=None):
+        w4a8.w4a8_gemm_lqq_bf16act(a, *lqq, n, out=outs[0], workspace=ws, stream=stream)
+        w4a8.w8a8_gemm_bf16act(a, *w8, n, out=outs[1], workspace=ws, stream=stream)
+        w4a8.w4a8_gemm_blockact(qb, sb, *w4, n, 32, out=outs[2], stream=stream)
+        w4a8.dequant_add_requant(qb, sb, x, 32, q_out=q_o, s_out=s_o, stream=stream)
+
+    run()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs] + [q_o.clone(), s_o.clone()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(torch.cuda.current_stream())
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        q_o.zero_()
+        s_o.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [o for o in outs] + [q_o, s_o]
+        for e, t in zip(eager, got):
+            assert torch.equal(e.view(torch.uint8), t.view(torch.uint8)), rep
