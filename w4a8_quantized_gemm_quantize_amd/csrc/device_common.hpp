@@ -180,6 +180,27 @@ __device__ __forceinline__ void global_to_lds16(const void *src, void *lds_block
     __builtin_amdgcn_global_load_lds((global_vptr)src, (lds_vptr)lds_block, 16, 0, 0);
 }
 
+// Raw (unstrided) buffer resource over [p, p + bytes).  A lane whose VGPR
+// offset is at or past `bytes` reads zero and touches no memory; the scalar
+// offset is added on top, so it must keep in-range lanes inside the buffer.
+// Word 3 = 0x00020000 is the 32-bit data format in the gfx9 descriptor
+// encoding, every other field zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+// 16 bytes per lane straight into LDS at lds_block + 16 * lane (m0 = lds_block).
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, void *lds_block,
+                                                int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)lds_block, 16, voff, soff, 0, 0);
+}
+
 // Byte offset of chunk j of n-tile t in the packed weights.
 __device__ __forceinline__ int64_t packed_chunk_offset(int64_t t, int64_t j, int64_t k) {
     return t * (int64_t)kNTile * k / 2 + j * kChunkBytes;
@@ -208,6 +229,25 @@ template <int WF>
 __device__ __forceinline__ uint32_t load_wparam(const uint8_t *p, int64_t idx) {
     if constexpr (WF == kW4Sym) return p[idx];
     else if constexpr (WF == kW4Lqq) return ((const uint16_t *)p)[idx];
+    else return 0u;
+}
+
+// The aligned 32-bit word that holds parameter idx, and the parameter taken
+// out of it.  A pipelined kernel keeps the word in flight across iterations:
+// a byte or halfword load would come back as a narrow value that the compiler
+// widens at the loop latch, which makes it wait for the load right there.
+// The parameter array is 16-byte aligned and a multiple of 16 bytes long, so
+// the word never leaves it.
+template <int WF>
+__device__ __forceinline__ uint32_t load_wparam_word(const uint8_t *p, int64_t idx) {
+    if constexpr (WF == kW4Sym) return ((const uint32_t *)p)[idx >> 2];
+    else if constexpr (WF == kW4Lqq) return ((const uint32_t *)p)[idx >> 1];
+    else return 0u;
+}
+template <int WF>
+__device__ __forceinline__ uint32_t wparam_from_word(uint32_t word, int64_t idx) {
+    if constexpr (WF == kW4Sym) return (word >> (8 * (int)(idx & 3))) & 0xffu;
+    else if constexpr (WF == kW4Lqq) return (word >> (16 * (int)(idx & 1))) & 0xffffu;
     else return 0u;
 }
 
@@ -264,6 +304,34 @@ __device__ __forceinline__ v4i wrec_operand(const WRec<WF> &rec, int h, uint32_t
         }
         return unpack_step(h ? rec.r.z : rec.r.x, h ? rec.r.w : rec.r.y, mul, add);
     }
+}
+
+// The rebuild constants straight from a parameter word (load_wparam_word):
+// per-lane v_perm_b32 selectors pick this channel's parameter bytes.
+//   kW4Sym  mul = s in bytes 0 and 2; add = 128 - 8 s in every byte, as one
+//           packed 16-bit multiply-add per half: (128 - 8 s) * 257 =
+//           32896 - 2056 s = s * (65536 - 2056) + 32896 (mod 2^16);
+//   kW4Lqq  mul = s in bytes 0 and 2; add = a in every byte.
+struct WParamSel { uint32_t mul, add; };
+template <int WF>
+__device__ __forceinline__ WParamSel wparam_selectors(int c) {
+    const uint32_t bs = WF == kW4Lqq ? 2u * (c & 1) : (uint32_t)(c & 3);
+    return WParamSel{bs | 0x0c00u | (bs << 16) | 0x0c000000u, (bs + 1u) * 0x01010101u};
+}
+template <int WF>
+__device__ __forceinline__ void wparam_consts(uint32_t word, WParamSel sel, uint32_t &mul,
+                                              uint32_t &add) {
+    mul = __builtin_amdgcn_perm(0u, word, sel.mul);
+    if constexpr (WF == kW4Lqq) add = __builtin_amdgcn_perm(0u, word, sel.add);
+    else add = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2u16, mul) *
+                                              v2u16{(uint16_t)(65536 - 2056), (uint16_t)(65536 - 2056)} +
+                                              v2u16{(uint16_t)32896, (uint16_t)32896});
+}
+template <int WF>
+__device__ __forceinline__ v4i wrec_operand_ma(const WRec<WF> &rec, int h, uint32_t mul,
+                                               uint32_t add) {
+    if constexpr (WF == kW8) return __builtin_bit_cast(v4i, h ? rec.r1 : rec.r0);
+    else return unpack_step(h ? rec.r.z : rec.r.x, h ? rec.r.w : rec.r.y, mul, add);
 }
 
 }  // namespace w4a8

@@ -543,7 +543,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     __shared__ __attribute__((aligned(16))) uint8_t wl1[L::kW];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    // readfirstlane: the compiler then knows the wavefront index is uniform,
+    // so LDS block addresses (m0 of the direct loads) stay in scalar registers.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     const int c = lane & 15;
 
@@ -564,74 +566,103 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     const int64_t n0 = (within / gsize) * BN;
     const int64_t t0 = n0 / kNTile;
     const int64_t ntiles = n / kNTile;
-    const int64_t nchunks = (k + kChunkK - 1) / kChunkK;
-    const int64_t G = k / kGroup;
 
-    // Activations of chunk j -> stage buf, global -> LDS directly
-    // (global_load_lds_dwordx4 fills one 1 KB block = 8 rows per instruction).
-    // Rows past m are clamped to row m - 1; they only reach unstored outputs.
-    // For the trailing 64-wide chunk the upper 64 columns are clamped into the
-    // row as well and never read.
-    auto issue_act = [&](int64_t j, auto buf_tag) {
+    // K in whole 128-wide chunks plus at most one trailing 64-wide chunk.  All
+    // indices and offsets below fit 32 bits: k <= K_MAX, and one workgroup
+    // reads at most BM k activation bytes and 16 BN k weight bytes (< 2^26).
+    const int ki = (int)k;
+    const int nchunks = (ki + kChunkK - 1) / kChunkK;
+    const int nfull = ki / kChunkK;
+    const int gk = ki / kGroup;
+    const std::integral_constant<bool, true> full_chunk;
+    const std::integral_constant<bool, false> half_chunk;
+
+    // Buffer resources over this workgroup's rows of A and tiles of W: rows
+    // past m and tiles past n read zero (they only reach unstored outputs), so
+    // no per-lane clamp is needed; each chunk's offset goes in a scalar.
+    constexpr int kWTileMul = WF == kW8 ? 16 : 8;                // weight bytes per tile = mul * k
+    constexpr int kPSize = WF == kW4Lqq ? 2 : 1;                 // bytes per group parameter
+    const int rows_here = (int)(m - m0 < BM ? m - m0 : BM);
+    const int tiles_here = (int)(ntiles - t0 < NTB ? ntiles - t0 : NTB);
+    const int wtile = kWTileMul * ki;
+    const int ptile = kNTile * gk * kPSize;
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(a_q + m0 * k, (uint32_t)rows_here * ki);
+    const __amdgpu_buffer_rsrc_t rw =
+        buffer_rsrc(w_packed + t0 * (int64_t)wtile, (uint32_t)tiles_here * wtile);
+    const __amdgpu_buffer_rsrc_t rp =
+        WF == kW8 ? rw : buffer_rsrc(grp_scale + t0 * (int64_t)ptile, (uint32_t)tiles_here * ptile);
+
+    // Activations of chunk j -> stage buf, buffer -> LDS directly (one 1 KB
+    // block = 8 rows of 128 bytes per instruction, 16-byte columns swizzled).
+    // For the trailing 64-wide chunk the upper 64 columns are folded onto the
+    // lower ones, so no load leaves the row; they are never read.
+    int aoff[ACT_I];
+#pragma unroll
+    for (int i = 0; i < ACT_I; ++i) {
+        const int row = (i * WAVES + wave) * 8 + (lane >> 3);
+        aoff[i] = row * ki + (act_swz(row, lane & 7) << 4);
+    }
+    auto issue_act = [&](int j, auto buf_tag, auto full_tag) {
         uint8_t *base = decltype(buf_tag)::value ? act1 : act0;
-        const bool full = (j + 1) * kChunkK <= k;
 #pragma unroll
         for (int i = 0; i < ACT_I; ++i) {
             const int blk = i * WAVES + wave;
-            const int row = blk * 8 + (lane >> 3);
-            int c16 = act_swz(row, lane & 7);   // the swizzle is its own inverse
-            if (!full) c16 &= 3;
-            const int64_t gm = (m0 + row < m) ? m0 + row : m - 1;
-            global_to_lds16(a_q + gm * k + j * kChunkK + c16 * 16, base + blk * 1024);
+            int off = aoff[i];
+            if constexpr (!decltype(full_tag)::value)
+                off -= (act_swz(blk * 8 + (lane >> 3), lane & 7) & 4) << 4;
+            buffer_to_lds16(ra, base + blk * 1024, off, j * kChunkK);
         }
     };
-    // Packed records and group parameters of this wavefront's tile(s) for
-    // chunk j, with a fixed number of unconditional loads whatever the chunk.
-    // Tiles past n are clamped to the last tile (outputs not stored).  A
-    // trailing 64-wide chunk of a 4-bit format has 8-byte records: the 16-byte
-    // window is clamped inside the 512-byte chunk and the wanted half picked
-    // after the load; its missing second group reuses the first group's
-    // parameter.  An int8 half chunk holds step 0 only, whose address is
-    // reloaded in place of step 1.
+    // Packed records and group-parameter words of this wavefront's tile(s) for
+    // chunk j.  A trailing 64-wide chunk of a 4-bit format has 8-byte records:
+    // the 16-byte window is kept inside the 512-byte chunk (lane 63 reads the
+    // last 16 bytes) and the wanted half picked at the rebuild; its missing
+    // second group reads the first group's word.  An int8 half chunk holds step
+    // 0 only, reloaded in place of step 1.
     //
     // Two register sets, by parity of the chunk index: the records of chunk
-    // j + 3 are requested while chunk j is multiplied, so each set has two
-    // iterations to arrive before its rebuild.  Requests past the last chunk
-    // are clamped to it (fetched, never used), so no branch surrounds them.
+    // j + 2 are requested at the start of iteration j, land during its MFMAs
+    // and are rebuilt in iteration j + 1.  Requests past the last chunk are
+    // clamped to it (fetched, never used).
+    int woff[TPW], woff_half[TPW], poff[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int tr = wave * TPW + i;
+        woff[i] = tr * wtile + lane * 16;
+        woff_half[i] = tr * wtile + (lane * 8 < 496 ? lane * 8 : 496);
+        poff[i] = tr * ptile + (WF == kW4Lqq ? (c & ~1) * 2 : (c & ~3));
+    }
+    const WParamSel psel = wparam_selectors<WF>(c);
     WRec<WF> wrec0[TPW], wrec1[TPW];
     uint32_t wsc0[TPW][2], wsc1[TPW][2];
-    constexpr int kWLoads = (WF == kW8 ? 2 : 3) * TPW;   // loads per fetch_w
-    auto fetch_w = [&](int64_t jreq, auto set_tag) {
+    auto fetch_w = [&](int jreq, auto set_tag) {
         WRec<WF>(&wrec)[TPW] = decltype(set_tag)::value ? wrec1 : wrec0;
         uint32_t(&wsc)[TPW][2] = decltype(set_tag)::value ? wsc1 : wsc0;
-        const int64_t j = jreq < nchunks ? jreq : nchunks - 1;
-        const bool wfull = (j + 1) * kChunkK <= k;
-        const int64_t g1 = wfull ? 2 * j + 1 : 2 * j;
+        const int j = jreq < nchunks ? jreq : nchunks - 1;
+        const bool wfull = j < nfull;
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
-            const int64_t t = (t0 + wave * TPW + i < ntiles) ? t0 + wave * TPW + i : ntiles - 1;
             if constexpr (WF == kW8) {
-                const uint8_t *base = w_packed + wchunk_offset<WF>(t, j, k) + lane * 16;
-                wrec[i].r0 = *(const u32x4 *)base;
-                wrec[i].r1 = *(const u32x4 *)(wfull ? base + kChunkBytes : base);
+                const int so = j * (2 * kChunkBytes);
+                wrec[i].r0 = buffer_load16(rw, woff[i], so);
+                wrec[i].r1 = buffer_load16(rw, woff[i], wfull ? so + kChunkBytes : so);
                 wsc[i][0] = wsc[i][1] = 0u;
             } else {
-                const int rec_off = wfull ? lane * 16 : (lane * 8 < 496 ? lane * 8 : 496);
-                wrec[i].r = *(const u32x4 *)(w_packed + packed_chunk_offset(t, j, k) + rec_off);
-                wsc[i][0] = load_wparam<WF>(grp_scale, t * kNTile * G + (2 * j) * kNTile + c);
-                wsc[i][1] = load_wparam<WF>(grp_scale, t * kNTile * G + g1 * kNTile + c);
+                wrec[i].r = buffer_load16(rw, wfull ? woff[i] : woff_half[i], j * kChunkBytes);
+                const int so = j * (2 * kNTile * kPSize);
+                wsc[i][0] = buffer_load4(rp, poff[i], so);
+                wsc[i][1] = buffer_load4(rp, poff[i], wfull ? so + kNTile * kPSize : so);
             }
         }
     };
     // Rebuild the int8 operands of both K steps of chunk j (from the register
     // set of its parity) into the LDS stage of the same parity.
-    auto rebuild_w = [&](int64_t j, auto buf_tag) {
+    auto rebuild_w = [&](auto buf_tag, auto full_tag) {
         uint8_t *wbase = decltype(buf_tag)::value ? wl1 : wl0;
         WRec<WF>(&wrec)[TPW] = decltype(buf_tag)::value ? wrec1 : wrec0;
         uint32_t(&wsc)[TPW][2] = decltype(buf_tag)::value ? wsc1 : wsc0;
-        const bool wfull = (j + 1) * kChunkK <= k;
         if constexpr (WF != kW8) {
-            if (!wfull) {
+            if constexpr (!decltype(full_tag)::value) {
 #pragma unroll
                 for (int i = 0; i < TPW; ++i)
                     wrec[i].r = (lane == 63) ? u32x4{wrec[i].r.z, wrec[i].r.w, 0u, 0u}
@@ -642,9 +673,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
         for (int i = 0; i < TPW; ++i) {
             const int tt = wave * TPW + i;
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < 2; ++h) {
+                uint32_t mul = 0u, add = 0u;
+                if constexpr (WF != kW8) wparam_consts<WF>(wsc[i][h], psel, mul, add);
                 *(v4i *)(wbase + ((tt * 2 + h) * 64 + lane) * 16) =
-                    wrec_operand<WF>(wrec[i], h, wsc[i][h]);
+                    wrec_operand_ma<WF>(wrec[i], h, mul, add);
+            }
         }
     };
 
@@ -742,47 +776,47 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     } while (0)
 
     // Pipeline over K chunks: iteration j multiplies stage `cur` while stage
-    // `nxt` is filled for chunk j + 1.  It issues the direct-to-LDS activation
-    // loads of chunk j + 1, runs the first K step of chunk j, rebuilds this
-    // wavefront's weight tile(s) of chunk j + 1 into `nxt` (records fetched
-    // two iterations earlier) while those MFMAs run, requests the records of
-    // chunk j + 3 into the register set just consumed, and runs the second K
-    // step.  The scheduling barriers keep that order, on which the barrier's
-    // wait count relies.
-    // The barrier at the end waits for everything but the last kWLoads
-    // requests (vmcnt completes in order): the activations of chunk j + 1 and
-    // the records of chunk j + 2 are in, the records of chunk j + 3 stay in
-    // flight.  (The LDS writes of the rebuild come first because the compiler
-    // makes any LDS store wait for direct-to-LDS loads still in flight.)
+    // `nxt` is filled for chunk j + 1.  All of its memory requests go out at
+    // its start: the direct-to-LDS activation loads of chunk j + 1 and the
+    // weight records of chunk j + 2.  It then runs the first K step of chunk j,
+    // rebuilds this wavefront's weight tile(s) of chunk j + 1 into `nxt` from
+    // records requested one iteration earlier, runs the second K step, and
+    // ends on a barrier that waits for every request of the iteration.  So a
+    // rebuild only reads registers that a barrier's wait already covered:
+    // with direct-to-LDS loads in flight the compiler cannot count vector
+    // loads in order, and any earlier use of a loaded register would make it
+    // wait for all of them, the activation loads just issued included.  The
+    // scheduling barriers keep the MFMAs of the first K step ahead of the
+    // rebuild's VALU work.
     const std::integral_constant<bool, false> stage0;
     const std::integral_constant<bool, true> stage1;
     if (nchunks > 0) {
         fetch_w(0, stage0);
         fetch_w(1, stage1);
-        rebuild_w(0, stage0);
-        fetch_w(2, stage0);
-        issue_act(0, stage0);
+        if (nfull > 0) {
+            rebuild_w(stage0, full_chunk);
+            issue_act(0, stage0, full_chunk);
+        } else {
+            rebuild_w(stage0, half_chunk);
+            issue_act(0, stage0, half_chunk);
+        }
         if constexpr (AB > 0) fetch_s(0, scur);
     }
     W4A8_LDS_BARRIER();
-    // lgkmcnt(0) and vmcnt(kWLoads) (expcnt left at its maximum)
-    constexpr int kPartialWait = (kWLoads & 15) | ((kWLoads >> 4) << 14) | 0x70;
-    static_assert(kWLoads < 64, "vmcnt field");
-    auto iteration = [&](int64_t j, auto cur, auto nxt) {
-        if (j + 1 < nchunks) issue_act(j + 1, nxt);
+    auto iteration = [&](int j, auto cur, auto nxt) {
+        if (j + 1 < nfull) issue_act(j + 1, nxt, full_chunk);
+        else if (j + 1 < nchunks) issue_act(j + 1, nxt, half_chunk);
+        fetch_w(j + 2, cur);
         if constexpr (AB > 0)
             if (j + 1 < nchunks) fetch_s(j + 1, snxt);
+        __builtin_amdgcn_sched_barrier(0);
         mma_step(cur, 0);
         __builtin_amdgcn_sched_barrier(0);
-        if (j + 1 < nchunks) rebuild_w(j + 1, nxt);
+        if (j + 1 < nfull) rebuild_w(nxt, full_chunk);
+        else if (j + 1 < nchunks) rebuild_w(nxt, half_chunk);
         __builtin_amdgcn_sched_barrier(0);
-        fetch_w(j + 3, nxt);
-        __builtin_amdgcn_sched_barrier(0);
-        if ((j + 1) * kChunkK <= k) mma_step(cur, 1);
-        __builtin_amdgcn_s_waitcnt(kPartialWait);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
+        if (j < nfull) mma_step(cur, 1);
+        W4A8_LDS_BARRIER();
         if constexpr (AB > 0) {
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm)
@@ -790,7 +824,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
                 for (int b = 0; b < NBC; ++b) scur[tm][b] = snxt[tm][b];
         }
     };
-    for (int64_t j = 0; j < nchunks; j += 2) {
+    for (int j = 0; j < nchunks; j += 2) {
         iteration(j, stage0, stage1);
         if (j + 1 < nchunks) iteration(j + 1, stage1, stage0);
     }
