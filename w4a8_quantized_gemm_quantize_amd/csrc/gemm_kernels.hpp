@@ -157,7 +157,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     __shared__ unsigned amax_lds[ROWS];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    // readfirstlane: the compiler then knows the wavefront index, and so each
+    // wavefront's chunk range and loop control, is uniform (scalar branches).
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int c = lane & 15, kq = lane >> 4;
     const int64_t ntiles = n / kNTile;
     const int64_t t0 = (int64_t)blockIdx.x * NT;
@@ -387,21 +389,33 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
             }
         }
     };
-    // Software pipeline over batches: the next batch is requested before the
-    // current one is used.  The request sits in the loop body with no branch
-    // around it (a conditional load would make the compiler's wait at the join
-    // cover the prefetched batch too), and the last batch is peeled.
+    // Software pipeline over batches with two register sets used in turn: the
+    // next batch is requested into the other set before the current one is
+    // used, so multiplying a batch waits only for its own loads while the next
+    // batch stays in flight (a copy from one set to the other would wait for
+    // both).  The scheduling barriers keep the requests ahead of the uses:
+    // the scheduler would otherwise sink them to reuse registers, exposing
+    // their latency.
+    WeightBatch<WF, NT, D, MT, !FUSED, AB> other;
     int64_t jb = j0;
-    for (; jb + D < j1; jb += D) {
-        WeightBatch<WF, NT, D, MT, !FUSED, AB> nxt;
-        load_batch(nxt, jb + D);
-        // keep the requests here: the scheduler would otherwise sink them below
-        // the uses of `cur` to reuse its registers, exposing their latency
+    while (true) {
+        if (jb + D >= j1) {
+            if (jb < j1) compute_batch(cur, jb, j1 - jb);
+            break;
+        }
+        load_batch(other, jb + D);
         __builtin_amdgcn_sched_barrier(0);
         compute_batch(cur, jb, D);
-        cur = nxt;
+        jb += D;
+        if (jb + D >= j1) {
+            compute_batch(other, jb, j1 - jb);
+            break;
+        }
+        load_batch(cur, jb + D);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_batch(other, jb, D);
+        jb += D;
     }
-    if (jb < j1) compute_batch(cur, jb, j1 - jb);
 
     if (has_half && wave == WAVES - 1) {
         // Trailing 64-wide chunk: one K step.
