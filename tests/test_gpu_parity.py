@@ -37,6 +37,7 @@ def announce(*what):
     (37, 4096, 8), (37, 4096, 16), (37, 4096, 32), (37, 4096, 64), (37, 4096, 128),
     (37, 4096, 256), (37, 4096, 512), (37, 4096, 1024), (11, 2048, 2048), (9, 96, 24),
     (5, 28672, 28672), (3, 40960, 40960), (1, 8, 8), (300, 256, 256),
+    (66, 4096, 4096), (7, 8192, 8192), (5, 8200, 8200), (4, 6144, 3072),
 ])
 def test_quantize_matches_oracle(w4a8, rows, cols, block):
     announce("quantize", rows, cols, block)

@@ -55,9 +55,55 @@ __global__ __launch_bounds__(256) void quant_pow2_kernel(const u32x4 *__restrict
     }
 }
 
-// Any block that is a multiple of 8: one 256-thread workgroup per block.  Up
-// to 256 * MAXV vectors stay in registers between the two phases; a longer
-// block is read a second time (from cache) for phase 2.
+// Blocks of up to 64 * V vectors (8 elements each), one wavefront per block and
+// four per workgroup: each lane holds V vectors, all requested before any is
+// used (indices past the block are clamped to its last vector and ignored), so
+// a lane has V loads in flight; the block maximum is a wavefront reduction with
+// no barrier.  Per-token rows up to 8192 elements take this path.
+template <int V>
+__global__ __launch_bounds__(256) void quant_row_wave_kernel(const u32x4 *__restrict__ x,
+                                                             int64_t nblocks, int block_vecs,
+                                                             u32x2 *__restrict__ q,
+                                                             float *__restrict__ scales) {
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    for (int64_t b = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); b < nblocks; b += nwaves) {
+        const u32x4 *xb = x + b * block_vecs;
+        u32x4 v[V];
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+            const int idx = lane + u * 64;
+            v[u] = __builtin_nontemporal_load(xb + (idx < block_vecs ? idx : block_vecs - 1));
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+            float f[8];
+            bf16x8_to_f32(v[u], f);
+            if (lane + u * 64 < block_vecs) amax = __builtin_fmaxf(amax, absmax_f32x8(f));
+        }
+        // amax >= 0 and never NaN, so its bits order like unsigned integers
+        amax = __uint_as_float(wave_max_u32(__float_as_uint(amax)));
+        float s, inv;
+        act_scale_pair(amax, s, inv);
+        u32x2 *qb = q + b * block_vecs;
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+            const int idx = lane + u * 64;
+            if (idx < block_vecs) {
+                float f[8];
+                bf16x8_to_f32(v[u], f);
+                __builtin_nontemporal_store(codes8(f, inv), qb + idx);
+            }
+        }
+        if (lane == 0) scales[b] = s;
+    }
+}
+
+// Longer blocks (any multiple of 8): one 256-thread workgroup per block.  Up to
+// 256 * MAXV vectors stay in registers between the two phases, all requested
+// before any is used (clamped indices, as above); a longer block is read a
+// second time (from cache) for phase 2.
 template <int MAXV>
 __global__ __launch_bounds__(256) void quant_wide_kernel(const u32x4 *__restrict__ x,
                                                          int64_t nblocks, int64_t block_vecs,
@@ -68,24 +114,24 @@ __global__ __launch_bounds__(256) void quant_wide_kernel(const u32x4 *__restrict
     for (int64_t b = blockIdx.x; b < nblocks; b += gridDim.x) {
         const int64_t base = b * block_vecs;
         u32x4 v[MAXV];
+#pragma unroll
+        for (int u = 0; u < MAXV; ++u) {
+            const int64_t idx = tid + (int64_t)u * 256;
+            v[u] = __builtin_nontemporal_load(&x[base + (idx < block_vecs ? idx : block_vecs - 1)]);
+        }
         float amax = 0.0f;
 #pragma unroll
         for (int u = 0; u < MAXV; ++u) {
-            int64_t idx = tid + (int64_t)u * 256;
-            if (idx < block_vecs) {
-                v[u] = x[base + idx];
-                float f[8];
-                bf16x8_to_f32(v[u], f);
-                amax = __builtin_fmaxf(amax, absmax_f32x8(f));
-            }
+            float f[8];
+            bf16x8_to_f32(v[u], f);
+            if (tid + (int64_t)u * 256 < block_vecs) amax = __builtin_fmaxf(amax, absmax_f32x8(f));
         }
         for (int64_t idx = tid + (int64_t)MAXV * 256; idx < block_vecs; idx += 256) {
             float f[8];
             bf16x8_to_f32(x[base + idx], f);
             amax = __builtin_fmaxf(amax, absmax_f32x8(f));
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
+        amax = __uint_as_float(wave_max_u32(__float_as_uint(amax)));
         if ((tid & 63) == 0) red[tid >> 6] = amax;
         __syncthreads();
         amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
@@ -94,11 +140,11 @@ __global__ __launch_bounds__(256) void quant_wide_kernel(const u32x4 *__restrict
         act_scale_pair(amax, s, inv);
 #pragma unroll
         for (int u = 0; u < MAXV; ++u) {
-            int64_t idx = tid + (int64_t)u * 256;
+            const int64_t idx = tid + (int64_t)u * 256;
             if (idx < block_vecs) {
                 float f[8];
                 bf16x8_to_f32(v[u], f);
-                q[base + idx] = codes8(f, inv);
+                __builtin_nontemporal_store(codes8(f, inv), &q[base + idx]);
             }
         }
         for (int64_t idx = tid + (int64_t)MAXV * 256; idx < block_vecs; idx += 256) {
@@ -171,9 +217,25 @@ hipError_t launch_quantize_act(const uint16_t *x, int64_t rows, int64_t cols, in
         case 512: quant_pow2_kernel<64><<<g, 256, 0, stream>>>(xv, nvec, qv, scales); break;
         default: {
             const int64_t nblocks = rows * (cols / block);
-            int64_t grid = nblocks < 65536 ? nblocks : 65536;
-            quant_wide_kernel<16><<<(int)grid, 256, 0, stream>>>(xv, nblocks, (int64_t)lpb, qv,
-                                                                 scales);
+            if (lpb <= 64 * 16) {
+                // one wavefront per block, four per workgroup
+                const int64_t wg = (nblocks + 3) / 4;
+                const int grid = (int)(wg < 65536 ? wg : 65536);
+                if (lpb <= 64)
+                    quant_row_wave_kernel<1><<<grid, 256, 0, stream>>>(xv, nblocks, lpb, qv, scales);
+                else if (lpb <= 128)
+                    quant_row_wave_kernel<2><<<grid, 256, 0, stream>>>(xv, nblocks, lpb, qv, scales);
+                else if (lpb <= 256)
+                    quant_row_wave_kernel<4><<<grid, 256, 0, stream>>>(xv, nblocks, lpb, qv, scales);
+                else if (lpb <= 512)
+                    quant_row_wave_kernel<8><<<grid, 256, 0, stream>>>(xv, nblocks, lpb, qv, scales);
+                else
+                    quant_row_wave_kernel<16><<<grid, 256, 0, stream>>>(xv, nblocks, lpb, qv, scales);
+            } else {
+                const int grid = (int)(nblocks < 65536 ? nblocks : 65536);
+                quant_wide_kernel<16><<<grid, 256, 0, stream>>>(xv, nblocks, (int64_t)lpb, qv,
+                                                                scales);
+            }
         }
     }
     return hipGetLastError();
