@@ -140,7 +140,11 @@ struct WeightBatch {
 // AV: 16-byte activation vectors per thread in the fused prologue (unused otherwise).
 // AB: 0 = per-token activation scales a_scale[m]; 32, 64 or 128 = per-block
 // scales a_scale[m][k / AB] folded per block (non-fused form only).
-template <int WF, int MT, int NT, int WAVES, int D, bool FUSED, int AV, int AB = 0>
+// KF: the fused prologue keeps the widened activations in registers between its
+// maximum and its codes (fewer VALU instructions, more registers: used when one
+// workgroup per CU is all the grid has, so occupancy does not matter).
+template <int WF, int MT, int NT, int WAVES, int D, bool FUSED, int AV, int AB = 0,
+          bool KF = false>
 __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     const void *__restrict__ act, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ w_packed, const uint8_t *__restrict__ grp_scale,
@@ -252,13 +256,23 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
         // for the weights, which stream in while the prologue runs.
         load_batch(cur, j0);
         lds_barrier();  // red / amax_lds cleared
+        // With KF each vector is widened once and the floats are kept for the
+        // codes below.  When the row splits evenly over its threads (every
+        // vector valid) the per-vector range checks are skipped.
+        const bool all_valid = KF && row_ok && tpr * AV == vpr;
+        float fa[KF ? AV : 1][8];
         float amax = 0.0f;
 #pragma unroll
         for (int u = 0; u < AV; ++u) {
             float f[8];
             bf16x8_to_f32(av[u], f);
             const float mx = absmax_f32x8(f);
-            if (row_ok && sub + (int64_t)u * tpr < vpr) amax = __builtin_fmaxf(amax, mx);
+            if constexpr (KF) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) fa[u][i] = f[i];
+            }
+            if (all_valid || (row_ok && sub + (int64_t)u * tpr < vpr))
+                amax = __builtin_fmaxf(amax, mx);
         }
         // amax >= 0 and never NaN, so its bits order like unsigned integers.
         float inv;
@@ -293,9 +307,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 #pragma unroll
             for (int u = 0; u < AV; ++u) {
                 const int64_t v = sub + (int64_t)u * tpr;
-                if (v < vpr) {
+                if (all_valid || v < vpr) {
                     float f[8];
-                    bf16x8_to_f32(av[u], f);
+                    if constexpr (KF) {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) f[i] = fa[u][i];
+                    } else {
+                        bf16x8_to_f32(av[u], f);
+                    }
                     const u32x2 q = codes8(f, inv);
                     *(u32x2 *)(act_lds + row * lds_stride + v * 8) = q;
                     if (blockIdx.x == 0) *(u32x2 *)(ws_q + row * k + v * 8) = q;
@@ -922,7 +941,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     }
 }
 
-template <int WF, int MT, int NT, bool FUSED, int AV = 1, int AB = 0, int FW = 8>
+template <int WF, int MT, int NT, bool FUSED, int AV = 1, int AB = 0, int FW = 8, bool KF = false>
 void launch_skinny(const void *act, const float *a_scale, const uint8_t *w_packed,
                    const uint8_t *grp_scale, const float *ch_scale, int64_t m, int64_t n,
                    int64_t k, void *out, int out_dtype, int8_t *ws_q, float *ws_s,
@@ -935,7 +954,7 @@ void launch_skinny(const void *act, const float *a_scale, const uint8_t *w_packe
                             : (MT == 1 ? 4 : (MT == 2 ? 2 : (NT == 1 && AB == 0 ? 2 : 1)));
     const int64_t ntiles = n / kNTile;
     const unsigned grid = (unsigned)((ntiles + NT - 1) / NT);
-    gemm_skinny_kernel<WF, MT, NT, WAVES, D, FUSED, AV, AB><<<grid, 64 * WAVES, dyn_lds,
+    gemm_skinny_kernel<WF, MT, NT, WAVES, D, FUSED, AV, AB, KF><<<grid, 64 * WAVES, dyn_lds,
                                                             stream>>>(
         act, a_scale, w_packed, grp_scale, ch_scale, (int)m, n, k, out, out_dtype, ws_q, ws_s);
 }
@@ -1065,7 +1084,17 @@ hipError_t launch_gemm_bf16act_fmt(const uint16_t *a, const uint8_t *w_packed,
     if (av > 0) {
         const size_t lds_bytes = (size_t)(m * (k + 16));
         const bool w16 = fused_waves(k) == 16;
-        if (av == 4 && w16)
+        int dev = 0, ncu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            ncu = 0;
+        // one workgroup per 16-channel tile: at most one per CU -> keep the floats
+        const bool one_per_cu = n / kNTile <= (int64_t)ncu;
+        if (av == 4 && w16 && one_per_cu)
+            launch_skinny<WF, 1, 1, true, 4, 0, 16, true>(a, nullptr, w_packed, grp_scale, ch_scale,
+                                                          m, n, k, out, out_dtype, ws_q, ws_s,
+                                                          lds_bytes, stream);
+        else if (av == 4 && w16)
             launch_skinny<WF, 1, 1, true, 4, 0, 16>(a, nullptr, w_packed, grp_scale, ch_scale, m,
                                                     n, k, out, out_dtype, ws_q, ws_s, lds_bytes,
                                                     stream);
