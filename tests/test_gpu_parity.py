@@ -139,6 +139,8 @@ GEMM_SHAPES = [
     (200, 272, 384),    # ragged M and N
     (256, 512, 1024),
     (129, 144, 4160),   # K = 32.5 chunks
+    (37, 8192, 1088),   # skinny path with row splits (>= 512 tiles), ragged M, half chunk
+    (64, 8208, 640),    # row splits, odd tile count (last workgroup half empty)
 ]
 
 
@@ -156,7 +158,7 @@ def test_gemm_int32_accumulator_bit_exact(w4a8, m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(16, 256, 256), (5, 48, 192), (65, 48, 192),
-                                   (200, 272, 384), (8, 4096, 4096)])
+                                   (200, 272, 384), (8, 4096, 4096), (50, 8192, 576)])
 def test_gemm_float_outputs(w4a8, m, n, k):
     announce("gemm f32/bf16", m, n, k)
     _, dev_w, ref_w = _pack(w4a8, n, k, seed=3 * m + n)
