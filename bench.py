@@ -191,7 +191,11 @@ def main():
     gss = [gs0] + [gs0.clone() for _ in range(copies - 1)]
     css = [cs0] + [cs0.clone() for _ in range(copies - 1)]
     acts = [a0] + [a0.clone() for _ in range(copies - 1)]
-    wss = [torch.empty(w4a8.workspace_bytes(m, k), dtype=torch.uint8, device=dev)
+    # codes and scales of the quantized activations, then (16 < m <= 64, large K)
+    # the int32 partial sums of the split-K GEMM
+    ws_base = w4a8.workspace_bytes(m, k)
+    split = w4a8.gemm_workspace_bytes(m, n, k) > 0
+    wss = [torch.empty(w4a8.workspace_bytes(m, k, n), dtype=torch.uint8, device=dev)
            for _ in range(copies)]
     out = torch.empty((m, n), dtype=out_dtype, device=dev)
 
@@ -202,7 +206,11 @@ def main():
 
     def gemm_only(r, stream):
         a_q, a_s = w4a8.workspace_views(wss[r], m, k)
-        w4a8.w4a8_gemm(a_q, a_s, wps[r], gss[r], css[r], n, out=out, stream=stream)
+        if split:
+            w4a8.w4a8_gemm_ws(a_q, a_s, wps[r], gss[r], css[r], n, out=out,
+                              workspace=wss[r][ws_base:], stream=stream)
+        else:
+            w4a8.w4a8_gemm(a_q, a_s, wps[r], gss[r], css[r], n, out=out, stream=stream)
 
     # Warm up eagerly on a side stream, then capture `copies` steps (one per
     # weight copy) into one HIP graph; the timed region replays it.
@@ -239,7 +247,8 @@ def main():
 
     # Dominant kernel: with m <= 16 the step is one fused kernel (quantization in
     # the GEMM's prologue), so its average duration is the step time; otherwise
-    # the GEMM launches alone are replayed from their own graph and timed.
+    # the GEMM launches alone are replayed from their own graph and timed (with
+    # split K: the K-sliced GEMM and the pass that sums its partials, together).
     fused = m <= 16
     if fused:
         gemm_ms = ms_per_step
@@ -268,8 +277,16 @@ def main():
         achieved = ops / (gemm_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
                 "frac": achieved / INT8_PEAK_TOPS}
-    kernel_key = ("gemm_skinny_fused" if fused else "gemm_skinny") if hbm_bound else "gemm_tiled"
+    if split:
+        kernel_key = "gemm_splitk"
+    elif hbm_bound:
+        kernel_key = "gemm_skinny_fused" if fused else "gemm_skinny"
+    else:
+        kernel_key = "gemm_tiled"
     roof["kernel"] = kernel_key
+    if split:
+        roof["kernel_launches"] = ["gemm_tiled_kernel over K slices", "splitk_finalize_kernel"]
+        roof["splitk_partial_bytes"] = w4a8.gemm_workspace_bytes(m, n, k)
     roof["kernel_ms"] = gemm_ms
     roof["algorithmic_bytes_per_launch"] = gemm_bytes
     roof["traffic"] = profile_traffic(kernel_key, args.workload)

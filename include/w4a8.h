@@ -165,6 +165,29 @@ w4a8_status w4a8_gemm(const int8_t *a_q, const float *a_scale, const uint8_t *w_
                       hipStream_t stream);
 
 /*
+ * Bytes of optional scratch that lets w4a8_gemm_ws (and the fused entry points
+ * below) split K over workgroups for an m x n x k product: int32 partial sums,
+ * for 16 < m <= 64 (decode-batch shapes whose one-pass kernel re-reads all of
+ * A in every workgroup).  0 when that shape is not split.  Part of the GEMM
+ * design choices, not of the method: the result is the same bit for bit.
+ */
+size_t w4a8_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
+/*
+ * w4a8_gemm with an optional workspace (16-byte aligned device memory owned by
+ * the caller, contents undefined on entry and after the call).  When
+ * w4a8_gemm_workspace_bytes(m, n, k) > 0 the workspace is required
+ * (W4A8_ERR_NULL / W4A8_ERR_MISALIGNED / W4A8_ERR_SHAPE if null, misaligned or
+ * smaller) and the product splits K; otherwise it is ignored and may be null.
+ * Same arguments, rules and result as w4a8_gemm.  Calls that share a workspace
+ * must be ordered (one stream).
+ */
+w4a8_status w4a8_gemm_ws(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
+                         const uint8_t *grp_scale, const float *ch_scale, int64_t m, int64_t n,
+                         int64_t k, int32_t group, void *out, w4a8_dtype out_dtype,
+                         void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Bytes of workspace w4a8_gemm_bf16act needs for m rows of k activations:
  * the int8 codes [m, k] at offset 0, then the binary32 per-row scales [m] at
  * offset round_up(m * k, 256).
@@ -176,7 +199,9 @@ size_t w4a8_gemm_bf16act_workspace_bytes(int64_t m, int64_t k);
  * (quantize_act_blockwise with block == k) into `workspace`, then w4a8_gemm.
  * The result equals those two calls bit for bit; the workspace holds the
  * activation codes and scales afterwards (layout above).  ws_bytes must be
- * at least w4a8_gemm_bf16act_workspace_bytes(m, k) (W4A8_ERR_SHAPE).
+ * at least w4a8_gemm_bf16act_workspace_bytes(m, k) (W4A8_ERR_SHAPE).  When it
+ * also has w4a8_gemm_workspace_bytes(m, n, k) > 0 bytes after that, they hold
+ * the split-K partials (as for w4a8_gemm_ws).
  * Requires k > 0 and the w4a8_gemm shape rules.
  */
 w4a8_status w4a8_gemm_bf16act(const uint16_t *a, const uint8_t *w_packed,

@@ -58,7 +58,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ["quantize_act_blockwise", "dequantize_act_blockwise", "pack_w4_grouped",
                  "unpack_w4_grouped", "w4a8_gemm", "w4a8_gemm_bf16act",
-                 "w4a8_gemm_bf16act_workspace_bytes", "w4a8_abi_version",
+                 "w4a8_gemm_bf16act_workspace_bytes", "w4a8_gemm_workspace_bytes",
+                 "w4a8_gemm_ws", "w4a8_abi_version",
                  "w4a8_pack_layout_version", "w4a8_status_string"]:
         assert want in names
 
@@ -146,6 +147,46 @@ def test_bf16act_workspace_and_validation(lib):
     assert f(A, B, C, D, 8, 64, 4096, 64, E, 1, MIS, need, NUL) == ERR_MISALIGNED
     assert f(A, B, C, D, 8, 64, 0, 64, E, 1, A, need, NUL) == ERR_SHAPE    # k == 0
     assert f(A, B, C, D, 8, 64, 4096, 32, E, 1, A, need, NUL) == ERR_UNSUPPORTED
+
+
+def splitk_bytes_expected(m, n, k):
+    """Split-K scratch size restated from its definition: for 16 < m <= 64 and at
+    least two whole 128-wide chunks, S = min(ceil(512 / ceil(n / 128)), k // 128,
+    16) slices of whole chunks, split only if S >= 2 and 32 S m <= k; one int32
+    [m, n] slice per slice of K actually used."""
+    if m <= 16 or m > 64 or k < 256:
+        return 0
+    ntb = -(-n // 128)
+    s = min(-(-512 // ntb), k // 128, 16)
+    if s < 2 or 32 * s * m > k:
+        return 0
+    kslice = -(-(k // 128) // s) * 128
+    return -(-k // kslice) * m * n * 4
+
+
+def test_gemm_ws_workspace_and_validation(lib):
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    ws = lib.w4a8_gemm_workspace_bytes
+    ws.argtypes = [I64, I64, I64]
+    ws.restype = ctypes.c_size_t
+    for m, n, k in [(64, 8192, 28672), (37, 8192, 1088), (17, 256, 4096), (64, 48, 512),
+                    (16, 8192, 28672), (65, 8192, 4096), (40, 4096, 128), (0, 64, 256),
+                    (33, 8208, 640), (20, 16384, 2624), (17, 32768, 1216),
+                    (64, 28672, 8192), (24, 14352, 4096), (48, 8192, 8192)]:
+        assert ws(m, n, k) == splitk_bytes_expected(m, n, k), (m, n, k)
+    assert ws(64, 8192, 28672) == 8 * 64 * 8192 * 4       # 8 slices of 28 chunks
+    assert ws(20, 16384, 2624) == 5 * 20 * 16384 * 4      # 4 x 5 chunks + a half-chunk slice
+    assert ws(48, 8192, 8192) == 0                        # partials would outweigh the gain
+    assert ws(64, 8192, 4096) == 0
+    g = lib.w4a8_gemm_ws
+    g.argtypes = [P, P, P, P, P, I64, I64, I64, I32, P, ctypes.c_int, P, ctypes.c_size_t, P]
+    need = ws(64, 8192, 28672)
+    assert need > 0
+    assert g(A, B, C, D, E, 64, 8192, 28672, 64, A, 1, NUL, need, NUL) == ERR_NULL
+    assert g(A, B, C, D, E, 64, 8192, 28672, 64, A, 1, MIS, need, NUL) == ERR_MISALIGNED
+    assert g(A, B, C, D, E, 64, 8192, 28672, 64, A, 1, A, need - 1, NUL) == ERR_SHAPE
+    assert g(A, B, C, D, E, 64, 8192, 28672, 128, A, 1, A, need, NUL) == ERR_UNSUPPORTED
+    assert g(NUL, NUL, NUL, NUL, NUL, 0, 64, 256, 64, NUL, 1, NUL, 0, NUL) == OK   # m == 0
 
 
 @pytest.fixture(scope="module")

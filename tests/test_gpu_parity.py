@@ -157,6 +157,77 @@ def test_gemm_int32_accumulator_bit_exact(w4a8, m, n, k):
     assert np.array_equal(acc.cpu().numpy(), acc_ref)
 
 
+# Split K (16 < m <= 64 with a workspace): the K slices, their int32 partials and
+# the summing pass must reproduce the one-pass result exactly.
+SPLITK_SHAPES = [
+    (20, 16384, 2624),  # 4 slices of 5 chunks and a fifth of the trailing half chunk only
+    (17, 32768, 1216),  # 2 slices, the second ending on a half chunk
+    (24, 14352, 4096),  # N ragged against the 128-wide tile, 5 slices
+    (33, 8208, 8448),   # M ragged in the 64-row tile, on the split threshold, 8 slices
+    (64, 8192, 28672),  # 70B-like FFN down, M = 64: 8 slices
+    (64, 28672, 8192),  # 70B-like FFN up shape, M = 64: 3 slices
+]
+
+
+@pytest.mark.parametrize("m,n,k", SPLITK_SHAPES)
+def test_gemm_splitk_int32_bit_exact(w4a8, m, n, k):
+    announce("gemm split-K i32", m, n, k)
+    assert w4a8.gemm_workspace_bytes(m, n, k) > 0
+    _, dev_w, ref_w = _pack(w4a8, n, k, seed=m + 2 * n)
+    a = inputs.activations(m, k, seed=m + 1, outlier_frac=0.001)
+    a_q, a_s = oracle.quantize_act_blockwise(a, k)
+    acc = w4a8.w4a8_gemm_ws(torch.from_numpy(a_q).cuda(),
+                            torch.from_numpy(a_s.reshape(-1)).cuda(), *dev_w, n,
+                            out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    acc_ref, _ = oracle.w4a8_gemm(a_q, a_s, *ref_w, 64, want_y=False)
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+
+
+@pytest.mark.parametrize("m,n,k", SPLITK_SHAPES[:4] + [(48, 8192, 8192), (64, 48, 512)])
+def test_gemm_splitk_equals_one_pass(w4a8, m, n, k):
+    # the last two are not split (partials would outweigh the gain; one column
+    # tile): w4a8_gemm_ws then takes the one-pass path
+    announce("gemm split-K vs one pass", m, n, k)
+    _, dev_w, _ = _pack(w4a8, n, k, seed=5 * m + n)
+    a = inputs.activations(m, k, seed=3 * m, outlier_frac=0.001)
+    q, s = w4a8.quantize_act_blockwise(to_dev_bf16(a), k)
+    s = s.reshape(-1)
+    need = w4a8.gemm_workspace_bytes(m, n, k)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    for dt in (torch.float32, torch.bfloat16, torch.int32):
+        y1 = w4a8.w4a8_gemm(q, s, *dev_w, n, out_dtype=dt)
+        y2 = w4a8.w4a8_gemm_ws(q, s, *dev_w, n, out_dtype=dt, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int32) if dt != torch.bfloat16 else y1.view(torch.int16),
+                           y2.view(torch.int32) if dt != torch.bfloat16 else y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("fmt", ["w4", "lqq", "w8"])
+def test_fused_splitk_workspace_equals_without(w4a8, fmt):
+    """The fused entry points split K when the workspace has room for the partials;
+    the result, and the codes and scales left in the workspace, do not change."""
+    m, n, k = 24, 14352, 4096
+    announce("fused split-K", fmt, m, n, k)
+    w = to_dev_bf16(inputs.weights(n, k, seed=17))
+    a = to_dev_bf16(inputs.activations(m, k, seed=19, outlier_frac=0.001))
+    if fmt == "w4":
+        packed, fn = w4a8.pack_w4_grouped(w), w4a8.w4a8_gemm_bf16act
+    elif fmt == "lqq":
+        packed, fn = w4a8.pack_w4_lqq(w), w4a8.w4a8_gemm_lqq_bf16act
+    else:
+        packed, fn = w4a8.pack_w8_channel(w), w4a8.w8a8_gemm_bf16act
+    small = torch.empty(w4a8.workspace_bytes(m, k), dtype=torch.uint8, device="cuda")
+    big = torch.empty(w4a8.workspace_bytes(m, k, n), dtype=torch.uint8, device="cuda")
+    assert big.numel() > small.numel()
+    y1 = fn(a, *packed, n, out_dtype=torch.bfloat16, workspace=small)
+    y2 = fn(a, *packed, n, out_dtype=torch.bfloat16, workspace=big)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    for v1, v2 in zip(w4a8.workspace_views(small, m, k), w4a8.workspace_views(big, m, k)):
+        assert torch.equal(v1.view(torch.uint8), v2.view(torch.uint8))
+
+
 @pytest.mark.parametrize("m,n,k", [(16, 256, 256), (5, 48, 192), (65, 48, 192),
                                    (200, 272, 384), (8, 4096, 4096), (50, 8192, 576)])
 def test_gemm_float_outputs(w4a8, m, n, k):

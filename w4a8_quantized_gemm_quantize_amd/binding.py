@@ -42,6 +42,9 @@ _SIGS = {
     "unpack_w4_grouped": ([_P, _P, _I64, _I64, _I32, _P, _P, _P], ctypes.c_int),
     "w4a8_gemm": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, ctypes.c_int, _P],
                   ctypes.c_int),
+    "w4a8_gemm_workspace_bytes": ([_I64, _I64, _I64], ctypes.c_size_t),
+    "w4a8_gemm_ws": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, ctypes.c_int, _P,
+                      ctypes.c_size_t, _P], ctypes.c_int),
     "w4a8_gemm_bf16act_workspace_bytes": ([_I64, _I64], ctypes.c_size_t),
     "w4a8_gemm_bf16act": ([_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, ctypes.c_int, _P,
                            ctypes.c_size_t, _P], ctypes.c_int),
@@ -187,8 +190,35 @@ def w4a8_gemm(a_q, a_scale, w_packed, grp_scale, ch_scale, n: int, out_dtype=tor
     return out
 
 
-def workspace_bytes(m: int, k: int) -> int:
-    return int(_lib.w4a8_gemm_bf16act_workspace_bytes(m, k))
+def gemm_workspace_bytes(m: int, n: int, k: int) -> int:
+    """Split-K scratch of w4a8_gemm_ws for an m x n x k product (0: not split)."""
+    return int(_lib.w4a8_gemm_workspace_bytes(m, n, k))
+
+
+def w4a8_gemm_ws(a_q, a_scale, w_packed, grp_scale, ch_scale, n: int,
+                 out_dtype=torch.bfloat16, group: int = GROUP, out=None, workspace=None,
+                 stream=None):
+    """w4a8_gemm with a caller workspace that lets 16 < m <= 64 split K (same result)."""
+    _dev(a_q, torch.int8, "a_q")
+    m, k = a_q.shape
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a_q.device)
+    need = gemm_workspace_bytes(m, n, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=a_q.device)
+    _check("w4a8_gemm_ws",
+           _lib.w4a8_gemm_ws(_ptr(a_q), _ptr(a_scale), _ptr(w_packed), _ptr(grp_scale),
+                             _ptr(ch_scale), m, n, k, group, _ptr(out), _OUT[out.dtype],
+                             _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                             _stream(stream)))
+    return out
+
+
+def workspace_bytes(m: int, k: int, n: int = None) -> int:
+    """Workspace of the fused entry points: codes and scales, plus (given n) the
+    split-K partials that let 16 < m <= 64 split K."""
+    base = int(_lib.w4a8_gemm_bf16act_workspace_bytes(m, k))
+    return base + (gemm_workspace_bytes(m, n, k) if n is not None else 0)
 
 
 def w4a8_gemm_bf16act(a, w_packed, grp_scale, ch_scale, n: int, out_dtype=torch.bfloat16,
@@ -198,7 +228,7 @@ def w4a8_gemm_bf16act(a, w_packed, grp_scale, ch_scale, n: int, out_dtype=torch.
     m, k = a.shape
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=a.device)
-    need = workspace_bytes(m, k)
+    need = workspace_bytes(m, k, n)
     if workspace is None:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=a.device)
     _check("w4a8_gemm_bf16act",
@@ -266,7 +296,7 @@ def w4a8_gemm_lqq_bf16act(a, w_packed, grp_param, ch_scale, n: int, out_dtype=to
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=a.device)
     if workspace is None:
-        workspace = torch.empty((max(workspace_bytes(m, k), 16),), dtype=torch.uint8,
+        workspace = torch.empty((max(workspace_bytes(m, k, n), 16),), dtype=torch.uint8,
                                 device=a.device)
     _check("w4a8_gemm_lqq_bf16act",
            _lib.w4a8_gemm_lqq_bf16act(_ptr(a), _ptr(w_packed), _ptr(grp_param), _ptr(ch_scale),
@@ -314,7 +344,7 @@ def w8a8_gemm_bf16act(a, w_packed, ch_scale, n: int, out_dtype=torch.bfloat16, o
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=a.device)
     if workspace is None:
-        workspace = torch.empty((max(workspace_bytes(m, k), 16),), dtype=torch.uint8,
+        workspace = torch.empty((max(workspace_bytes(m, k, n), 16),), dtype=torch.uint8,
                                 device=a.device)
     _check("w8a8_gemm_bf16act",
            _lib.w8a8_gemm_bf16act(_ptr(a), _ptr(w_packed), _ptr(ch_scale), m, n, k, _ptr(out),

@@ -66,20 +66,22 @@ w4a8_status check_gemm_args(const void *a, const float *a_scale, bool need_a_sca
     return W4A8_OK;
 }
 
-// Workspace checks of the fused entry points; on success sets the code and
-// scale pointers inside it.
-w4a8_status split_workspace(void *workspace, size_t ws_bytes, int64_t m, int64_t k,
-                            int8_t **a_q, float **a_s);
-
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-w4a8_status split_workspace(void *workspace, size_t ws_bytes, int64_t m, int64_t k,
-                            int8_t **a_q, float **a_s) {
+// Workspace checks of the fused entry points; on success sets the code and
+// scale pointers inside it, and the split-K partials when the workspace also
+// has w4a8_gemm_workspace_bytes(m, n, k) > 0 bytes after them (else null).
+w4a8_status split_workspace(void *workspace, size_t ws_bytes, int64_t m, int64_t n, int64_t k,
+                            int8_t **a_q, float **a_s, int32_t **partials) {
     if (!workspace) return W4A8_ERR_NULL;
     if (!aligned16(workspace)) return W4A8_ERR_MISALIGNED;
-    if (ws_bytes < w4a8_gemm_bf16act_workspace_bytes(m, k)) return W4A8_ERR_SHAPE;
+    const size_t base = w4a8_gemm_bf16act_workspace_bytes(m, k);
+    if (ws_bytes < base) return W4A8_ERR_SHAPE;
     *a_q = (int8_t *)workspace;
     *a_s = (float *)((uint8_t *)workspace + round_up((size_t)m * (size_t)k, 256));
+    const size_t extra = w4a8::splitk_partial_bytes(m, n, k);
+    *partials = (extra > 0 && ws_bytes - base >= extra)
+                    ? (int32_t *)((uint8_t *)workspace + base) : nullptr;
     return W4A8_OK;
 }
 
@@ -165,6 +167,32 @@ w4a8_status w4a8_gemm(const int8_t *a_q, const float *a_scale, const uint8_t *w_
                   stream);
 }
 
+size_t w4a8_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+    if (m <= 0 || n <= 0 || k <= 0) return 0;
+    return w4a8::splitk_partial_bytes(m, n, k);
+}
+
+w4a8_status w4a8_gemm_ws(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
+                         const uint8_t *grp_scale, const float *ch_scale, int64_t m, int64_t n,
+                         int64_t k, int32_t group, void *out, w4a8_dtype out_dtype,
+                         void *workspace, size_t ws_bytes, hipStream_t stream) {
+    w4a8_status st = check_gemm_args(a_q, a_scale, true, w_packed, grp_scale, ch_scale, m, n,
+                                     k, group, out, out_dtype);
+    if (st != W4A8_OK) return st;
+    if (m == 0 || n == 0) return W4A8_OK;
+    const size_t need = w4a8_gemm_workspace_bytes(m, n, k);
+    int32_t *partials = nullptr;
+    if (need > 0) {
+        if (!workspace) return W4A8_ERR_NULL;
+        if (!aligned16(workspace)) return W4A8_ERR_MISALIGNED;
+        if (ws_bytes < need) return W4A8_ERR_SHAPE;
+        partials = (int32_t *)workspace;
+    }
+    return finish(w4a8::launch_w4a8_gemm(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k,
+                                         out, (int)out_dtype, stream, partials),
+                  stream);
+}
+
 size_t w4a8_gemm_bf16act_workspace_bytes(int64_t m, int64_t k) {
     if (m <= 0 || k <= 0) return 0;
     return round_up((size_t)m * (size_t)k, 256) + round_up((size_t)m * sizeof(float), 256);
@@ -182,10 +210,11 @@ w4a8_status w4a8_gemm_bf16act(const uint16_t *a, const uint8_t *w_packed,
     if (m == 0 || n == 0) return W4A8_OK;
     int8_t *a_q;
     float *a_s;
-    st = split_workspace(workspace, ws_bytes, m, k, &a_q, &a_s);
+    int32_t *partials;
+    st = split_workspace(workspace, ws_bytes, m, n, k, &a_q, &a_s, &partials);
     if (st != W4A8_OK) return st;
     return finish(w4a8::launch_w4a8_gemm_bf16act(a, w_packed, grp_scale, ch_scale, m, n, k, out,
-                                                 (int)out_dtype, a_q, a_s, stream),
+                                                 (int)out_dtype, a_q, a_s, stream, partials),
                   stream);
 }
 
@@ -245,10 +274,11 @@ w4a8_status w4a8_gemm_lqq_bf16act(const uint16_t *a, const uint8_t *w_packed,
     if (m == 0 || n == 0) return W4A8_OK;
     int8_t *a_q;
     float *a_s;
-    st = split_workspace(workspace, ws_bytes, m, k, &a_q, &a_s);
+    int32_t *partials;
+    st = split_workspace(workspace, ws_bytes, m, n, k, &a_q, &a_s, &partials);
     if (st != W4A8_OK) return st;
     return finish(w4a8::launch_w4a8_gemm_lqq_bf16act(a, w_packed, grp_param, ch_scale, m, n, k,
-                                                     out, (int)out_dtype, a_q, a_s, stream),
+                                                     out, (int)out_dtype, a_q, a_s, stream, partials),
                   stream);
 }
 
@@ -297,10 +327,11 @@ w4a8_status w8a8_gemm_bf16act(const uint16_t *a, const int8_t *w_packed, const f
     if (m == 0 || n == 0) return W4A8_OK;
     int8_t *a_q;
     float *a_s;
-    st = split_workspace(workspace, ws_bytes, m, k, &a_q, &a_s);
+    int32_t *partials;
+    st = split_workspace(workspace, ws_bytes, m, n, k, &a_q, &a_s, &partials);
     if (st != W4A8_OK) return st;
     return finish(w4a8::launch_w8a8_gemm_bf16act(a, w_packed, ch_scale, m, n, k, out,
-                                                 (int)out_dtype, a_q, a_s, stream),
+                                                 (int)out_dtype, a_q, a_s, stream, partials),
                   stream);
 }
 

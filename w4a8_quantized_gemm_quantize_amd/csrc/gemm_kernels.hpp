@@ -550,12 +550,16 @@ __device__ __forceinline__ int act_lds_off(int row, int c16) {
 
 // AB: 0 = per-token activation scales; 32, 64 or 128 = per-block scales
 // a_scale[m][k / AB], each block's int32 partial folded into binary32 in K order.
+// kslice (a multiple of 128): blockIdx.y = s takes K range [s kslice, (s + 1)
+// kslice) and writes its int32 partial sums (out_dtype 2) to slice s of `out`,
+// [gridDim.y][m][ldo]; one slice (kslice >= k) is the whole product.  Per-token
+// scales only when split.
 template <int WF, int BM, int BN, int WAVES_M, int WAVES_N, int AB = 0>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 : 1) void gemm_tiled_kernel(
     const int8_t *__restrict__ a_q, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ w_packed, const uint8_t *__restrict__ grp_scale,
     const float *__restrict__ ch_scale, int64_t m, int64_t n, int64_t k,
-    void *__restrict__ out, int64_t ldo, int out_dtype) {
+    void *__restrict__ out, int64_t ldo, int out_dtype, int64_t kslice) {
     using L = TiledLds<BM, BN>;
     constexpr int WAVES = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -600,13 +604,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     const int64_t t0 = n0 / kNTile;
     const int64_t ntiles = n / kNTile;
 
-    // K in whole 128-wide chunks plus at most one trailing 64-wide chunk.  All
-    // indices and offsets below fit 32 bits: k <= K_MAX, and one workgroup
-    // reads at most BM k activation bytes and 16 BN k weight bytes (< 2^26).
-    const int ki = (int)k;
+    // This workgroup's K slice: the operand pointers move to its first chunk
+    // (strides stay those of the whole K), its partials to slice blockIdx.y.
+    const int64_t k0 = (int64_t)blockIdx.y * kslice;
+    a_q += k0;
+    w_packed += (k0 / kChunkK) * (WF == kW8 ? 2 * kChunkBytes : kChunkBytes);
+    if (WF != kW8) grp_scale += (k0 / kGroup) * kNTile * (WF == kW4Lqq ? 2 : 1);
+    out = (uint8_t *)out + (int64_t)blockIdx.y * m * ldo * (out_dtype == 1 ? 2 : 4);
+    // K in whole 128-wide chunks plus at most one trailing 64-wide chunk (only
+    // in the last slice).  All indices and offsets below fit 32 bits: k <=
+    // K_MAX, and one workgroup reads at most BM k activation bytes and 16 BN k
+    // weight bytes (< 2^26).
+    const int kfull = (int)k;
+    const int ki = (int)(k - k0 < kslice ? k - k0 : kslice);   // this slice
     const int nchunks = (ki + kChunkK - 1) / kChunkK;
     const int nfull = ki / kChunkK;
-    const int gk = ki / kGroup;
+    const int gk = kfull / kGroup;
     const std::integral_constant<bool, true> full_chunk;
     const std::integral_constant<bool, false> half_chunk;
 
@@ -617,9 +630,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     constexpr int kPSize = WF == kW4Lqq ? 2 : 1;                 // bytes per group parameter
     const int rows_here = (int)(m - m0 < BM ? m - m0 : BM);
     const int tiles_here = (int)(ntiles - t0 < NTB ? ntiles - t0 : NTB);
-    const int wtile = kWTileMul * ki;
+    const int wtile = kWTileMul * kfull;
     const int ptile = kNTile * gk * kPSize;
-    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(a_q + m0 * k, (uint32_t)rows_here * ki);
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(a_q + m0 * k, (uint32_t)rows_here * kfull);
     const __amdgpu_buffer_rsrc_t rw =
         buffer_rsrc(w_packed + t0 * (int64_t)wtile, (uint32_t)tiles_here * wtile);
     const __amdgpu_buffer_rsrc_t rp =
@@ -633,7 +646,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
 #pragma unroll
     for (int i = 0; i < ACT_I; ++i) {
         const int row = (i * WAVES + wave) * 8 + (lane >> 3);
-        aoff[i] = row * ki + (act_swz(row, lane & 7) << 4);
+        aoff[i] = row * kfull + (act_swz(row, lane & 7) << 4);
     }
     auto issue_act = [&](int j, auto buf_tag, auto full_tag) {
         uint8_t *base = decltype(buf_tag)::value ? act1 : act0;
@@ -870,7 +883,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     // the stage arrays, then stores whole 128-byte row segments, so each output
     // cache line is written in full (straight from the accumulator layout a lane
     // holds only 4 consecutive columns of a row).  16-byte segments are
-    // XOR-swizzled by row % 8 for conflict-free reads.  Four-byte outputs go in
+    // XOR-swizzled by the row (mod 8, or mod the segments per row when a row
+    // has fewer) for conflict-free reads.  Four-byte outputs go in
     // two passes of half the rows.
     {
         constexpr int PER_ARRAY = WAVES / 4;
@@ -884,7 +898,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
         const int which = wave / PER_ARRAY;
         uint8_t *ebuf = (which == 0 ? act0 : which == 1 ? act1 : which == 2 ? wl0 : wl1) +
                         (wave % PER_ARRAY) * (WM * WN * 2);
-        auto seg_off = [&](int r, int seg) { return r * row_bytes + ((seg ^ (r & 7)) << 4); };
+        // the XOR stays inside the row: segs is a power of two, 2 to 16
+        const int swz_mask = (segs < 8 ? segs : 8) - 1;
+        auto seg_off = [&](int r, int seg) {
+            return r * row_bytes + ((seg ^ (r & swz_mask)) << 4);
+        };
         for (int pass = 0; pass < WM / rows_pass; ++pass) {
             // accumulators -> LDS (lane (c, kq): row tm * 16 + c, 4 columns)
 #pragma unroll
@@ -960,23 +978,101 @@ void launch_skinny(const void *act, const float *a_scale, const uint8_t *w_packe
 }
 
 // Output columns [n_off, n_off + n_sub) of an [m, ldo] product: the weight
-// pointers move by whole 16-channel tiles (tile-major layouts).
+// pointers move by whole 16-channel tiles (tile-major layouts).  kslice > 0
+// splits K into ceil(k / kslice) slices of int32 partials (see the kernel).
 template <int WF, int BM, int BN, int WAVES_M, int WAVES_N, int AB = 0>
 void launch_tiled_cols(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
                        const uint8_t *grp_scale, const float *ch_scale, int64_t m, int64_t n_off,
                        int64_t n_sub, int64_t ldo, int64_t k, void *out, int out_dtype,
-                       hipStream_t stream) {
+                       hipStream_t stream, int64_t kslice = 0) {
     if (n_sub <= 0) return;
+    if (kslice <= 0 || kslice >= k) kslice = k;
     const int64_t t_off = n_off / kNTile;
     const int64_t wtile = WF == kW8 ? kNTile * k : kNTile * k / 2;      // bytes per tile
     const int64_t ptile = kNTile * (k / kGroup) * (WF == kW4Lqq ? 2 : 1);  // parameter bytes
     const int esize = out_dtype == 1 ? 2 : 4;
     const int64_t grid = ((m + BM - 1) / BM) * ((n_sub + BN - 1) / BN);
-    gemm_tiled_kernel<WF, BM, BN, WAVES_M, WAVES_N, AB><<<(unsigned)grid,
+    // k == 0: one slice of no chunks (the product is zero)
+    const unsigned slices = kslice > 0 ? (unsigned)((k + kslice - 1) / kslice) : 1u;
+    gemm_tiled_kernel<WF, BM, BN, WAVES_M, WAVES_N, AB><<<dim3((unsigned)grid, slices),
                                                           64 * WAVES_M * WAVES_N, 0, stream>>>(
         a_q, a_scale, w_packed + t_off * wtile,
         grp_scale ? grp_scale + t_off * ptile : grp_scale, ch_scale + n_off, m, n_sub, k,
-        (uint8_t *)out + n_off * esize, ldo, out_dtype);
+        (uint8_t *)out + n_off * esize, ldo, out_dtype, kslice);
+}
+
+// ------------------------------------------------------------- split K --
+// The skinny kernel's wavefronts split K inside one workgroup per 16-channel
+// tile, so every workgroup reads all of A: at m = 64, k = 28672 that is 470 MB
+// of activation loads for 117 MB of weights, and the vector-memory address
+// path of the CUs, not HBM, sets the time.  With a caller workspace, 16 < m <=
+// 64 instead runs 64 x 128 output tiles of the tiled kernel (A shared by its 8
+// wavefronts through LDS) over S slices of K, each slice writing int32
+// partials, then a pass that sums the slices (exact, any order) and applies
+// the same binary32 epilogue as the one-pass kernels.
+constexpr int kSplitBM = 64, kSplitBN = 128;
+
+// Slices of K for an m x n x k split-K product (0: not split).  About 512
+// workgroups (two per CU: one alone leaves too few loads in flight), at most
+// 16 slices of at least one chunk.  The partials cost 8 S m n bytes (written,
+// then read) against n k / 2 bytes of 4-bit weights, so K is split only while
+// that stays within half the weights (32 S m <= k); below it the one-pass
+// kernel is faster (e.g. m = 48, n = k = 8192).
+inline int64_t splitk_slices(int64_t m, int64_t n, int64_t k) {
+    if (m <= 16 || m > 64 || k < 2 * kChunkK) return 0;
+    const int64_t ntb = (n + kSplitBN - 1) / kSplitBN;
+    int64_t s = (512 + ntb - 1) / ntb;
+    const int64_t nfull = k / kChunkK;
+    if (s > nfull) s = nfull;
+    if (s > 16) s = 16;
+    if (s < 2 || 32 * s * m > k) return 0;
+    return s;
+}
+inline int64_t splitk_kslice(int64_t k, int64_t s) {
+    const int64_t nfull = k / kChunkK;
+    return ((nfull + s - 1) / s) * kChunkK;             // whole chunks per slice
+}
+// Bytes of int32 partials (0 when the shape is not split).
+inline size_t splitk_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+    const int64_t s = splitk_slices(m, n, k);
+    if (s == 0) return 0;
+    const int64_t used = (k + splitk_kslice(k, s) - 1) / splitk_kslice(k, s);
+    return (size_t)used * (size_t)m * (size_t)n * 4;
+}
+
+// out[r][c..c+3] from the sum of `slices` int32 partial slices [slices][m][n].
+__global__ __launch_bounds__(256) void splitk_finalize_kernel(const v4i *__restrict__ part,
+                                                              int slices, int64_t m, int64_t n,
+                                                              const float *__restrict__ a_scale,
+                                                              const float *__restrict__ ch_scale,
+                                                              void *__restrict__ out, int out_dtype) {
+    const int64_t quads = m * (n / 4);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < quads; q += stride) {
+        v4i acc = part[q];
+        for (int s = 1; s < slices; ++s) {
+            const v4i p = part[s * quads + q];
+            acc = v4i{acc[0] + p[0], acc[1] + p[1], acc[2] + p[2], acc[3] + p[3]};
+        }
+        const int64_t row = q / (n / 4), col = (q - row * (n / 4)) * 4;
+        store4(out, out_dtype, row, n, col, acc, a_scale[row], *(const f32x4 *)(ch_scale + col));
+    }
+}
+
+template <int WF>
+void launch_splitk(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
+                   const uint8_t *grp_scale, const float *ch_scale, int64_t m, int64_t n,
+                   int64_t k, void *out, int out_dtype, int32_t *partials, hipStream_t stream) {
+    const int64_t s = splitk_slices(m, n, k);
+    const int64_t kslice = splitk_kslice(k, s);
+    const int slices = (int)((k + kslice - 1) / kslice);
+    launch_tiled_cols<WF, kSplitBM, kSplitBN, 1, 8>(a_q, a_scale, w_packed, grp_scale, ch_scale, m,
+                                                    0, n, n, k, partials, 2, stream, kslice);
+    const int64_t quads = m * (n / 4);
+    int64_t grid = (quads + 255) / 256;
+    if (grid > 4096) grid = 4096;
+    splitk_finalize_kernel<<<(unsigned)grid, 256, 0, stream>>>((const v4i *)partials, slices, m, n,
+                                                               a_scale, ch_scale, out, out_dtype);
 }
 
 template <int WF, int BM, int BN, int WAVES_M, int WAVES_N, int AB = 0>
@@ -1042,10 +1138,14 @@ template <int WF>
 hipError_t launch_gemm_fmt(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
                             const uint8_t *grp_scale, const float *ch_scale, int64_t m,
                             int64_t n, int64_t k, void *out, int out_dtype,
-                            hipStream_t stream) {
+                            hipStream_t stream, int32_t *partials = nullptr) {
     if (m == 0 || n == 0) return hipSuccess;
     const int64_t ntiles = n / kNTile;
-    if (k < kChunkK) {
+    if (partials && splitk_slices(m, n, k) > 0) {
+        // caller workspace of splitk_workspace_bytes(m, n, k) for the partials
+        launch_splitk<WF>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k, out, out_dtype,
+                          partials, stream);
+    } else if (k < kChunkK) {
         // no full 128-wide chunk: the skinny kernel's loads assume one
         launch_tiled<WF, 128, 128, 2, 2>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k,
                                          out, out_dtype, stream);
@@ -1078,7 +1178,8 @@ template <int WF>
 hipError_t launch_gemm_bf16act_fmt(const uint16_t *a, const uint8_t *w_packed,
                                     const uint8_t *grp_scale, const float *ch_scale, int64_t m,
                                     int64_t n, int64_t k, void *out, int out_dtype,
-                                    int8_t *ws_q, float *ws_s, hipStream_t stream) {
+                                    int8_t *ws_q, float *ws_s, hipStream_t stream,
+                                    int32_t *partials = nullptr) {
     if (m == 0 || n == 0) return hipSuccess;
     const int av = fused_vectors(m, k);
     if (av > 0) {
@@ -1113,7 +1214,7 @@ hipError_t launch_gemm_bf16act_fmt(const uint16_t *a, const uint8_t *w_packed,
     hipError_t e = launch_quantize_act(a, m, k, (int32_t)k, ws_q, ws_s, stream);
     if (e != hipSuccess) return e;
     return launch_gemm_fmt<WF>(ws_q, ws_s, w_packed, grp_scale, ch_scale, m, n, k, out,
-                               out_dtype, stream);
+                               out_dtype, stream, partials);
 }
 
 // GEMM with per-block activation scales (AB = 32, 64 or 128) on int8

@@ -15,16 +15,22 @@ hipError_t launch_pack_w4(const uint16_t *w, int64_t n, int64_t k, uint8_t *w_pa
                           uint8_t *grp_scale, float *ch_scale, hipStream_t stream);
 hipError_t launch_unpack_w4(const uint8_t *w_packed, const uint8_t *grp_scale, int64_t n,
                             int64_t k, int8_t *q, uint8_t *s_g, hipStream_t stream);
-// out_dtype: 0 = binary32, 1 = bf16, 2 = int32 accumulator
+// out_dtype: 0 = binary32, 1 = bf16, 2 = int32 accumulator.
+// partials (optional, splitk_partial_bytes(m, n, k) bytes, 16-byte aligned):
+// int32 scratch that lets 16 < m <= 64 split K over workgroups; without it those
+// shapes run the one-pass skinny kernel.  Same result bit for bit either way.
+size_t splitk_partial_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_w4a8_gemm(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
                             const uint8_t *grp_scale, const float *ch_scale, int64_t m,
-                            int64_t n, int64_t k, void *out, int out_dtype, hipStream_t stream);
+                            int64_t n, int64_t k, void *out, int out_dtype, hipStream_t stream,
+                            int32_t *partials = nullptr);
 // Per-token quantization of bf16 activations into (ws_q, ws_s) and the GEMM;
 // small m runs both in one kernel.
 hipError_t launch_w4a8_gemm_bf16act(const uint16_t *a, const uint8_t *w_packed,
                                     const uint8_t *grp_scale, const float *ch_scale, int64_t m,
                                     int64_t n, int64_t k, void *out, int out_dtype,
-                                    int8_t *ws_q, float *ws_s, hipStream_t stream);
+                                    int8_t *ws_q, float *ws_s, hipStream_t stream,
+                                    int32_t *partials = nullptr);
 
 
 // LiquidGEMM's asymmetric LQQ weights (parameter s | (128 + min) << 8 per group).
@@ -36,12 +42,12 @@ hipError_t launch_unpack_w4_lqq(const uint8_t *w_packed, const uint16_t *grp_par
 hipError_t launch_w4a8_gemm_lqq(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
                                 const uint16_t *grp_param, const float *ch_scale, int64_t m,
                                 int64_t n, int64_t k, void *out, int out_dtype,
-                                hipStream_t stream);
+                                hipStream_t stream, int32_t *partials = nullptr);
 hipError_t launch_w4a8_gemm_lqq_bf16act(const uint16_t *a, const uint8_t *w_packed,
                                         const uint16_t *grp_param, const float *ch_scale,
                                         int64_t m, int64_t n, int64_t k, void *out,
                                         int out_dtype, int8_t *ws_q, float *ws_s,
-                                        hipStream_t stream);
+                                        hipStream_t stream, int32_t *partials = nullptr);
 
 // W8A8 comparison path: per-channel int8 weights in the kW8 layout.
 hipError_t launch_pack_w8(const uint16_t *w, int64_t n, int64_t k, int8_t *w_packed,
@@ -50,11 +56,11 @@ hipError_t launch_unpack_w8(const int8_t *w_packed, int64_t n, int64_t k, int8_t
                             hipStream_t stream);
 hipError_t launch_w8a8_gemm(const int8_t *a_q, const float *a_scale, const int8_t *w_packed,
                             const float *ch_scale, int64_t m, int64_t n, int64_t k, void *out,
-                            int out_dtype, hipStream_t stream);
+                            int out_dtype, hipStream_t stream, int32_t *partials = nullptr);
 hipError_t launch_w8a8_gemm_bf16act(const uint16_t *a, const int8_t *w_packed,
                                     const float *ch_scale, int64_t m, int64_t n, int64_t k,
                                     void *out, int out_dtype, int8_t *ws_q, float *ws_s,
-                                    hipStream_t stream);
+                                    hipStream_t stream, int32_t *partials = nullptr);
 
 // W4A8 GEMM with per-block activation scales a_scale[m][k / block], block in
 // {32, 64, 128}; out_dtype 0 (binary32) or 1 (bf16).
