@@ -52,12 +52,17 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
 
-// binary32 -> bf16 bits, round to nearest even; NaN kept as a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+// Two binary32 values -> packed bf16 bits (lo in bits 0-15), one
+// v_cvt_pk_bf16_f32: round to nearest even, subnormals kept, a NaN kept as the
+// quiet NaN with the same sign and top payload bits ((u >> 16) | 0x40).  That is
+// exactly u + 0x7fff + ((u >> 16) & 1), shifted right by 16, for every non-NaN
+// bit pattern u; the instruction was compared with that integer form on all
+// 2^32 inputs, NaNs included, with no difference.  As a vector conversion
+// there is no branch per value (the integer form's NaN test compiled to one).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // round-half-even of v, saturated to [-lim, lim]; NaN gives 0.

@@ -77,8 +77,8 @@ __device__ __forceinline__ void store4(void *out, int out_dtype, int64_t row, in
         y[i] = y[i] * sc[i];
     }
     if (out_dtype == 1) {
-        const u32x2 b = {f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16),
-                         f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16)};
+        const u32x2 b = {bf16x2_rne(y[0], y[1]),
+                         bf16x2_rne(y[2], y[3])};
         *(u32x2 *)((uint16_t *)out + idx) = b;
     } else {
         *(f32x4 *)((float *)out + idx) = f32x4{y[0], y[1], y[2], y[3]};
@@ -104,8 +104,8 @@ __device__ __forceinline__ void store4f(void *out, int out_dtype, int64_t row, i
 #pragma unroll
     for (int i = 0; i < 4; ++i) y[i] = f[i] * sc[i];
     if (out_dtype == 1) {
-        const u32x2 b = {f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16),
-                         f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16)};
+        const u32x2 b = {bf16x2_rne(y[0], y[1]),
+                         bf16x2_rne(y[2], y[3])};
         *(u32x2 *)((uint16_t *)out + idx) = b;
     } else {
         *(f32x4 *)((float *)out + idx) = f32x4{y[0], y[1], y[2], y[3]};
@@ -903,6 +903,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
         auto seg_off = [&](int r, int seg) {
             return r * row_bytes + ((seg ^ (r & swz_mask)) << 4);
         };
+        // channel scales of this lane's 4 columns per 16-column tile (clamped
+        // past n: those columns are not stored)
+        f32x4 scv[TN];
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            const int64_t nn = n0 + wn * WN + tn * 16 + 4 * kq;
+            scv[tn] = *(const f32x4 *)(ch_scale + (nn < n ? nn : n - 4));
+        }
         for (int pass = 0; pass < WM / rows_pass; ++pass) {
             // accumulators -> LDS (lane (c, kq): row tm * 16 + c, 4 columns)
 #pragma unroll
@@ -914,14 +922,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
 #pragma unroll
                 for (int tn = 0; tn < TN; ++tn) {
                     const int col = tn * 16 + 4 * kq;             // within the wavefront tile
-                    const int64_t nn = n0 + wn * WN + col;
                     const int byte = col * esize;
                     uint8_t *dst = ebuf + seg_off(r, byte >> 4) + (byte & 15);
                     const v4i a4 = acc[tn][tm];
                     if (!AB && out_dtype == 2) {
                         *(v4i *)dst = a4;
                     } else {
-                        const f32x4 sc = *(const f32x4 *)(ch_scale + (nn < n ? nn : n - 4));
+                        const f32x4 sc = scv[tn];
                         float y[4];
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
@@ -933,8 +940,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
                             }
                         }
                         if (out_dtype == 1)
-                            *(u32x2 *)dst = u32x2{f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16),
-                                                  f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16)};
+                            *(u32x2 *)dst = u32x2{bf16x2_rne(y[0], y[1]),
+                                                  bf16x2_rne(y[2], y[3])};
                         else
                             *(f32x4 *)dst = f32x4{y[0], y[1], y[2], y[3]};
                     }

@@ -175,10 +175,10 @@ __global__ __launch_bounds__(256) void dequant_kernel(const u32x2 *__restrict__ 
         }
         if (BF16) {
             u32x4 o;
-            o.x = f32_to_bf16_rne(f[0]) | (f32_to_bf16_rne(f[1]) << 16);
-            o.y = f32_to_bf16_rne(f[2]) | (f32_to_bf16_rne(f[3]) << 16);
-            o.z = f32_to_bf16_rne(f[4]) | (f32_to_bf16_rne(f[5]) << 16);
-            o.w = f32_to_bf16_rne(f[6]) | (f32_to_bf16_rne(f[7]) << 16);
+            o.x = bf16x2_rne(f[0], f[1]);
+            o.y = bf16x2_rne(f[2], f[3]);
+            o.z = bf16x2_rne(f[4], f[5]);
+            o.w = bf16x2_rne(f[6], f[7]);
             __builtin_nontemporal_store(o, &((u32x4 *)out)[i]);
         } else {
             f32x4 *o = (f32x4 *)out;
