@@ -569,6 +569,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     constexpr int ACT_I = BM / 8 / WAVES;     // 1 KB activation blocks per wavefront
     static_assert(TPW >= 1 && TPW * WAVES == NTB, "one or more weight tiles per wavefront");
     static_assert(ACT_I >= 1 && ACT_I * WAVES * 8 == BM, "activation blocks per wavefront");
+    // With the wavefronts side by side in N and one 16-channel tile each
+    // (WAVES_M == 1), a wavefront consumes only the tile it rebuilds: the
+    // rebuilt operands then stay in its registers and skip the LDS round trip
+    // (LDS writes are the slow side of LDS on gfx950).
+    constexpr bool kRegW = WAVES_M == 1 && TPW == 1 && TN == 1;
     // Each stage of each operand is its own array and the chunk loop is unrolled
     // by two so every access names its array statically: the direct-to-LDS
     // activation loads into one stage then provably never alias reads of the
@@ -702,7 +707,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
         }
     };
     // Rebuild the int8 operands of both K steps of chunk j (from the register
-    // set of its parity) into the LDS stage of the same parity.
+    // set of its parity) into the LDS stage of the same parity (kRegW: into the
+    // operand registers of that parity).
+    v4i wreg0[kRegW ? 2 : 1], wreg1[kRegW ? 2 : 1];
     auto rebuild_w = [&](auto buf_tag, auto full_tag) {
         uint8_t *wbase = decltype(buf_tag)::value ? wl1 : wl0;
         WRec<WF>(&wrec)[TPW] = decltype(buf_tag)::value ? wrec1 : wrec0;
@@ -722,8 +729,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
             for (int h = 0; h < 2; ++h) {
                 uint32_t mul = 0u, add = 0u;
                 if constexpr (WF != kW8) wparam_consts<WF>(wsc[i][h], psel, mul, add);
-                *(v4i *)(wbase + ((tt * 2 + h) * 64 + lane) * 16) =
-                    wrec_operand_ma<WF>(wrec[i], h, mul, add);
+                const v4i op = wrec_operand_ma<WF>(wrec[i], h, mul, add);
+                if constexpr (kRegW) {
+                    v4i(&wr)[2] = decltype(buf_tag)::value ? wreg1 : wreg0;
+                    wr[h] = op;
+                } else {
+                    *(v4i *)(wbase + ((tt * 2 + h) * 64 + lane) * 16) = op;
+                }
             }
         }
     };
@@ -768,9 +780,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm)
             av[tm] = *(const v4i *)(abase + act_lds_off(wm * WM + tm * 16 + c, 4 * h + kq));
+        if constexpr (kRegW) {
+            const v4i(&wr)[2] = decltype(buf_tag)::value ? wreg1 : wreg0;
+            wv[0] = wr[h];
+        } else {
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-            wv[tn] = *(const v4i *)(wbase + (((wn * TN + tn) * 2 + h) * 64 + lane) * 16);
+            for (int tn = 0; tn < TN; ++tn)
+                wv[tn] = *(const v4i *)(wbase + (((wn * TN + tn) * 2 + h) * 64 + lane) * 16);
+        }
         if constexpr (AB == 0) {
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn)
