@@ -569,11 +569,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     constexpr int ACT_I = BM / 8 / WAVES;     // 1 KB activation blocks per wavefront
     static_assert(TPW >= 1 && TPW * WAVES == NTB, "one or more weight tiles per wavefront");
     static_assert(ACT_I >= 1 && ACT_I * WAVES * 8 == BM, "activation blocks per wavefront");
-    // With the wavefronts side by side in N and one 16-channel tile each
-    // (WAVES_M == 1), a wavefront consumes only the tile it rebuilds: the
-    // rebuilt operands then stay in its registers and skip the LDS round trip
-    // (LDS writes are the slow side of LDS on gfx950).
-    constexpr bool kRegW = WAVES_M == 1 && TPW == 1 && TN == 1;
+    // With the wavefronts side by side in N (WAVES_M == 1) a wavefront consumes
+    // exactly the tiles whose records it fetches (TPW == TN).  Its weight
+    // operands are then rebuilt in registers right before their MFMAs and never
+    // pass through LDS (LDS writes are the slow side of LDS on gfx950); each
+    // tile is still rebuilt once per workgroup.
+    constexpr bool kRegW = WAVES_M == 1 && TPW == TN;
     // Each stage of each operand is its own array and the chunk loop is unrolled
     // by two so every access names its array statically: the direct-to-LDS
     // activation loads into one stage then provably never alias reads of the
@@ -673,8 +674,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     //
     // Two register sets, by parity of the chunk index: the records of chunk
     // j + 2 are requested at the start of iteration j, land during its MFMAs
-    // and are rebuilt in iteration j + 1.  Requests past the last chunk are
-    // clamped to it (fetched, never used).
+    // and are rebuilt in iteration j + 1 (kRegW: the records of chunk j + 1,
+    // used in iteration j + 1).  Requests past the last chunk are clamped to
+    // it (fetched, never used).
     int woff[TPW], woff_half[TPW], poff[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
@@ -706,22 +708,24 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
             }
         }
     };
+    // A trailing 64-wide chunk of a 4-bit format: pick this lane's 8-byte half
+    // of the 16-byte window (see above) into the step-0 words.
+    auto half_records = [&](auto set_tag) {
+        if constexpr (WF != kW8) {
+            WRec<WF>(&wrec)[TPW] = decltype(set_tag)::value ? wrec1 : wrec0;
+#pragma unroll
+            for (int i = 0; i < TPW; ++i)
+                wrec[i].r = (lane == 63) ? u32x4{wrec[i].r.z, wrec[i].r.w, 0u, 0u}
+                                         : u32x4{wrec[i].r.x, wrec[i].r.y, 0u, 0u};
+        }
+    };
     // Rebuild the int8 operands of both K steps of chunk j (from the register
-    // set of its parity) into the LDS stage of the same parity (kRegW: into the
-    // operand registers of that parity).
-    v4i wreg0[kRegW ? 2 : 1], wreg1[kRegW ? 2 : 1];
+    // set of its parity) into the LDS stage of the same parity.
     auto rebuild_w = [&](auto buf_tag, auto full_tag) {
         uint8_t *wbase = decltype(buf_tag)::value ? wl1 : wl0;
         WRec<WF>(&wrec)[TPW] = decltype(buf_tag)::value ? wrec1 : wrec0;
         uint32_t(&wsc)[TPW][2] = decltype(buf_tag)::value ? wsc1 : wsc0;
-        if constexpr (WF != kW8) {
-            if constexpr (!decltype(full_tag)::value) {
-#pragma unroll
-                for (int i = 0; i < TPW; ++i)
-                    wrec[i].r = (lane == 63) ? u32x4{wrec[i].r.z, wrec[i].r.w, 0u, 0u}
-                                             : u32x4{wrec[i].r.x, wrec[i].r.y, 0u, 0u};
-            }
-        }
+        if constexpr (!decltype(full_tag)::value) half_records(buf_tag);
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const int tt = wave * TPW + i;
@@ -729,13 +733,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
             for (int h = 0; h < 2; ++h) {
                 uint32_t mul = 0u, add = 0u;
                 if constexpr (WF != kW8) wparam_consts<WF>(wsc[i][h], psel, mul, add);
-                const v4i op = wrec_operand_ma<WF>(wrec[i], h, mul, add);
-                if constexpr (kRegW) {
-                    v4i(&wr)[2] = decltype(buf_tag)::value ? wreg1 : wreg0;
-                    wr[h] = op;
-                } else {
-                    *(v4i *)(wbase + ((tt * 2 + h) * 64 + lane) * 16) = op;
-                }
+                *(v4i *)(wbase + ((tt * 2 + h) * 64 + lane) * 16) =
+                    wrec_operand_ma<WF>(wrec[i], h, mul, add);
             }
         }
     };
@@ -781,8 +780,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
         for (int tm = 0; tm < TM; ++tm)
             av[tm] = *(const v4i *)(abase + act_lds_off(wm * WM + tm * 16 + c, 4 * h + kq));
         if constexpr (kRegW) {
-            const v4i(&wr)[2] = decltype(buf_tag)::value ? wreg1 : wreg0;
-            wv[0] = wr[h];
+            const WRec<WF>(&wrec)[TPW] = decltype(buf_tag)::value ? wrec1 : wrec0;
+            const uint32_t(&wsc)[TPW][2] = decltype(buf_tag)::value ? wsc1 : wsc0;
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                uint32_t mul = 0u, add = 0u;
+                if constexpr (WF != kW8) wparam_consts<WF>(wsc[tn][h], psel, mul, add);
+                wv[tn] = wrec_operand_ma<WF>(wrec[tn], h, mul, add);
+            }
         } else {
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn)
@@ -855,12 +860,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     const std::integral_constant<bool, true> stage1;
     if (nchunks > 0) {
         fetch_w(0, stage0);
-        fetch_w(1, stage1);
+        if constexpr (!kRegW) fetch_w(1, stage1);
         if (nfull > 0) {
-            rebuild_w(stage0, full_chunk);
+            if constexpr (!kRegW) rebuild_w(stage0, full_chunk);
             issue_act(0, stage0, full_chunk);
         } else {
-            rebuild_w(stage0, half_chunk);
+            if constexpr (!kRegW) rebuild_w(stage0, half_chunk);
             issue_act(0, stage0, half_chunk);
         }
         if constexpr (AB > 0) fetch_s(0, scur);
@@ -887,9 +892,28 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
                 for (int b = 0; b < NBC; ++b) scur[tm][b] = snxt[tm][b];
         }
     };
+    // kRegW: iteration j requests the activations and the weight records of
+    // chunk j + 1 (into the other stage and register set), then multiplies
+    // chunk j with its operands rebuilt in registers from the records of its
+    // set, which the previous barrier's wait covered.
+    auto iteration_rw = [&](int j, auto cur, auto nxt) {
+        if (j + 1 < nfull) issue_act(j + 1, nxt, full_chunk);
+        else if (j + 1 < nchunks) issue_act(j + 1, nxt, half_chunk);
+        fetch_w(j + 1, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j >= nfull) half_records(cur);
+        mma_step(cur, 0);
+        if (j < nfull) mma_step(cur, 1);
+        W4A8_LDS_BARRIER();
+    };
     for (int j = 0; j < nchunks; j += 2) {
-        iteration(j, stage0, stage1);
-        if (j + 1 < nchunks) iteration(j + 1, stage1, stage0);
+        if constexpr (kRegW) {
+            iteration_rw(j, stage0, stage1);
+            if (j + 1 < nchunks) iteration_rw(j + 1, stage1, stage0);
+        } else {
+            iteration(j, stage0, stage1);
+            if (j + 1 < nchunks) iteration(j + 1, stage1, stage0);
+        }
     }
     // the clamped requests past the last chunk: done before the stages are reused
     W4A8_LDS_BARRIER();
@@ -910,10 +934,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
         const int rows_pass = (esize == 2) ? WM : WM / 2;
         const int row_bytes = WN * esize;
         const int segs = row_bytes / 16;                 // 16-byte segments per row
-        static_assert(WM * WN * 2 <= (L::kW < L::kAct ? L::kW : L::kAct) / PER_ARRAY,
+        // kRegW: the weight stages held no operands; half the wavefronts use each
+        constexpr int PER_W = WAVES / 2;
+        static_assert(kRegW ? WM * WN * 2 * PER_W <= L::kW
+                            : WM * WN * 2 <= (L::kW < L::kAct ? L::kW : L::kAct) / PER_ARRAY,
                       "epilogue tile fits the stage arrays");
         const int which = wave / PER_ARRAY;
-        uint8_t *ebuf = (which == 0 ? act0 : which == 1 ? act1 : which == 2 ? wl0 : wl1) +
+        uint8_t *ebuf =
+            kRegW ? (wave < PER_W ? wl0 : wl1) + (wave % PER_W) * (WM * WN * 2)
+                  : (which == 0 ? act0 : which == 1 ? act1 : which == 2 ? wl0 : wl1) +
                         (wave % PER_ARRAY) * (WM * WN * 2);
         // the XOR stays inside the row: segs is a power of two, 2 to 16
         const int swz_mask = (segs < 8 ? segs : 8) - 1;
