@@ -352,7 +352,9 @@ def _sampled_check(w4a8, name, n_rows=48, n_cols=96, seed=0):
     announce("workload", name, m, n, k)
     wp, gs, cs = w4a8.pack_w4_grouped(to_dev_bf16(w))
     ad = to_dev_bf16(a)
-    ws = torch.empty(w4a8.workspace_bytes(m, k), dtype=torch.uint8, device="cuda")
+    # the workspace bench.py gives the step: codes, scales and (16 < m <= 64,
+    # large K) room for the split-K partials
+    ws = torch.empty(w4a8.workspace_bytes(m, k, n), dtype=torch.uint8, device="cuda")
     y = w4a8.w4a8_gemm_bf16act(ad, wp, gs, cs, n, out_dtype=torch.bfloat16, workspace=ws)
     acc = w4a8.w4a8_gemm_bf16act(ad, wp, gs, cs, n, out_dtype=torch.int32)
     torch.cuda.synchronize()
@@ -385,14 +387,18 @@ def test_large_workload_sampled(w4a8, name):
 
 # ------------------------------------------------------------ HIP graphs ----
 
-@pytest.mark.parametrize("m,n,k", [(8, 4096, 4096), (200, 256, 512)])
+@pytest.mark.parametrize("m,n,k", [(8, 4096, 4096), (200, 256, 512), (20, 16384, 2624)])
 def test_graph_replay_matches_eager(w4a8, m, n, k):
     """Library calls captured into a HIP graph (as the benchmark does) replay to the
-    eager result every time, with eager work and synchronizations in between."""
+    eager result every time, with eager work and synchronizations in between.
+    (20, 16384, 2624) runs the split-K pair of launches in the graph."""
     announce("graph replay", m, n, k)
     _, dev_w, _ = _pack(w4a8, n, k, seed=21)
     a = to_dev_bf16(inputs.activations(m, k, seed=21, outlier_frac=0.001))
-    ws = torch.empty(w4a8.workspace_bytes(m, k), dtype=torch.uint8, device="cuda")
+    base = w4a8.workspace_bytes(m, k)
+    split = w4a8.gemm_workspace_bytes(m, n, k) > 0
+    assert split == (m == 20)
+    ws = torch.empty(w4a8.workspace_bytes(m, k, n), dtype=torch.uint8, device="cuda")
     out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
     acc = torch.empty((m, n), dtype=torch.int32, device="cuda")
     eager = w4a8.w4a8_gemm_bf16act(a, *dev_w, n, out_dtype=torch.bfloat16).clone()
@@ -407,7 +413,10 @@ def test_graph_replay_matches_eager(w4a8, m, n, k):
     with torch.cuda.graph(g):
         w4a8.w4a8_gemm_bf16act(a, *dev_w, n, out=out, workspace=ws)
         ws_q, ws_s = w4a8.workspace_views(ws, m, k)
-        w4a8.w4a8_gemm(ws_q, ws_s, *dev_w, n, out=acc)
+        if split:
+            w4a8.w4a8_gemm_ws(ws_q, ws_s, *dev_w, n, out=acc, workspace=ws[base:])
+        else:
+            w4a8.w4a8_gemm(ws_q, ws_s, *dev_w, n, out=acc)
     for rep in range(4):
         out.zero_()
         acc.fill_(-1)
