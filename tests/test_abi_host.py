@@ -172,10 +172,11 @@ def test_gemm_ws_workspace_and_validation(lib):
     for m, n, k in [(64, 8192, 28672), (37, 8192, 1088), (17, 256, 4096), (64, 48, 512),
                     (16, 8192, 28672), (65, 8192, 4096), (40, 4096, 128), (0, 64, 256),
                     (33, 8208, 640), (20, 16384, 2624), (17, 32768, 1216),
-                    (64, 28672, 8192), (24, 14352, 4096), (48, 8192, 8192)]:
+                    (64, 28672, 8192), (24, 14352, 4096), (48, 8192, 8192), (17, 256, 10304)]:
         assert ws(m, n, k) == splitk_bytes_expected(m, n, k), (m, n, k)
     assert ws(64, 8192, 28672) == 8 * 64 * 8192 * 4       # 8 slices of 28 chunks
     assert ws(20, 16384, 2624) == 5 * 20 * 16384 * 4      # 4 x 5 chunks + a half-chunk slice
+    assert ws(17, 256, 10304) == 17 * 17 * 256 * 4        # 16 x 5 chunks + a half-chunk slice
     assert ws(48, 8192, 8192) == 0                        # partials would outweigh the gain
     assert ws(64, 8192, 4096) == 0
     g = lib.w4a8_gemm_ws

@@ -166,6 +166,7 @@ SPLITK_SHAPES = [
     (33, 8208, 8448),   # M ragged in the 64-row tile, on the split threshold, 8 slices
     (64, 8192, 28672),  # 70B-like FFN down, M = 64: 8 slices
     (64, 28672, 8192),  # 70B-like FFN up shape, M = 64: 3 slices
+    (17, 256, 10304),   # 16 slices of 5 chunks plus a 17th of the trailing half chunk
 ]
 
 

@@ -1093,7 +1093,11 @@ inline size_t splitk_workspace_bytes(int64_t m, int64_t n, int64_t k) {
     return (size_t)used * (size_t)m * (size_t)n * 4;
 }
 
-// out[r][c..c+3] from the sum of `slices` int32 partial slices [slices][m][n].
+// out[r][c..c+3] from the sum of the int32 partial slices [slices][m][n].  With
+// S > 0 the count is a template argument (S == slices), so a thread's S loads
+// are all in flight before the first add; a runtime trip count (S == 0) left
+// them one round trip apart.
+template <int S>
 __global__ __launch_bounds__(256) void splitk_finalize_kernel(const v4i *__restrict__ part,
                                                               int slices, int64_t m, int64_t n,
                                                               const float *__restrict__ a_scale,
@@ -1102,13 +1106,44 @@ __global__ __launch_bounds__(256) void splitk_finalize_kernel(const v4i *__restr
     const int64_t quads = m * (n / 4);
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < quads; q += stride) {
-        v4i acc = part[q];
-        for (int s = 1; s < slices; ++s) {
-            const v4i p = part[s * quads + q];
-            acc = v4i{acc[0] + p[0], acc[1] + p[1], acc[2] + p[2], acc[3] + p[3]};
+        v4i acc;
+        if constexpr (S > 0) {
+            v4i p[S];
+#pragma unroll
+            for (int s = 0; s < S; ++s) p[s] = part[s * quads + q];
+            acc = p[0];
+#pragma unroll
+            for (int s = 1; s < S; ++s)
+                acc = v4i{acc[0] + p[s][0], acc[1] + p[s][1], acc[2] + p[s][2], acc[3] + p[s][3]};
+        } else {
+            acc = part[q];
+            for (int s = 1; s < slices; ++s) {
+                const v4i p = part[s * quads + q];
+                acc = v4i{acc[0] + p[0], acc[1] + p[1], acc[2] + p[2], acc[3] + p[3]};
+            }
         }
         const int64_t row = q / (n / 4), col = (q - row * (n / 4)) * 4;
         store4(out, out_dtype, row, n, col, acc, a_scale[row], *(const f32x4 *)(ch_scale + col));
+    }
+}
+
+// Unrolled forms for 2..17 slices (splitk_slices gives at most 16, plus one
+// slice for a trailing half chunk); any other count takes the runtime loop.
+template <int S>
+void launch_finalize(const int32_t *partials, int slices, int64_t m, int64_t n,
+                     const float *a_scale, const float *ch_scale, void *out, int out_dtype,
+                     unsigned grid, hipStream_t stream) {
+    if constexpr (S > 17) {
+        splitk_finalize_kernel<0><<<grid, 256, 0, stream>>>((const v4i *)partials, slices, m, n,
+                                                            a_scale, ch_scale, out, out_dtype);
+    } else {
+        if (slices == S)
+            splitk_finalize_kernel<S><<<grid, 256, 0, stream>>>((const v4i *)partials, slices, m,
+                                                                n, a_scale, ch_scale, out,
+                                                                out_dtype);
+        else
+            launch_finalize<S + 1>(partials, slices, m, n, a_scale, ch_scale, out, out_dtype, grid,
+                                   stream);
     }
 }
 
@@ -1124,8 +1159,8 @@ void launch_splitk(const int8_t *a_q, const float *a_scale, const uint8_t *w_pac
     const int64_t quads = m * (n / 4);
     int64_t grid = (quads + 255) / 256;
     if (grid > 4096) grid = 4096;
-    splitk_finalize_kernel<<<(unsigned)grid, 256, 0, stream>>>((const v4i *)partials, slices, m, n,
-                                                               a_scale, ch_scale, out, out_dtype);
+    launch_finalize<2>(partials, slices, m, n, a_scale, ch_scale, out, out_dtype, (unsigned)grid,
+                       stream);
 }
 
 template <int WF, int BM, int BN, int WAVES_M, int WAVES_N, int AB = 0>
