@@ -582,8 +582,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     // wait for the loads in flight.
     __shared__ __attribute__((aligned(16))) uint8_t act0[L::kAct];
     __shared__ __attribute__((aligned(16))) uint8_t act1[L::kAct];
-    __shared__ __attribute__((aligned(16))) uint8_t wl0[L::kW];
-    __shared__ __attribute__((aligned(16))) uint8_t wl1[L::kW];
+    // kRegW: a third activation stage (the K loop runs two chunks ahead), and
+    // the weight arrays only stage the epilogue (half the wavefronts each).
+    constexpr int kEpiW = (WAVES / 2) * WM * WN * 2;
+    __shared__ __attribute__((aligned(16))) uint8_t act2[kRegW ? L::kAct : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t wl0[kRegW ? kEpiW : L::kW];
+    __shared__ __attribute__((aligned(16))) uint8_t wl1[kRegW ? kEpiW : L::kW];
 
     const int tid = threadIdx.x;
     // readfirstlane: the compiler then knows the wavefront index is uniform,
@@ -654,8 +658,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
         const int row = (i * WAVES + wave) * 8 + (lane >> 3);
         aoff[i] = row * kfull + (act_swz(row, lane & 7) << 4);
     }
+    // Stage and register-set selection by a compile-time tag (0, 1 or 2).
+    auto act_of = [&](auto st) -> uint8_t * {
+        constexpr int S = (int)decltype(st)::value;
+        if constexpr (S == 0) return act0;
+        else if constexpr (S == 1) return act1;
+        else return act2;
+    };
     auto issue_act = [&](int j, auto buf_tag, auto full_tag) {
-        uint8_t *base = decltype(buf_tag)::value ? act1 : act0;
+        uint8_t *base = act_of(buf_tag);
 #pragma unroll
         for (int i = 0; i < ACT_I; ++i) {
             const int blk = i * WAVES + wave;
@@ -674,9 +685,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     //
     // Two register sets, by parity of the chunk index: the records of chunk
     // j + 2 are requested at the start of iteration j, land during its MFMAs
-    // and are rebuilt in iteration j + 1 (kRegW: the records of chunk j + 1,
-    // used in iteration j + 1).  Requests past the last chunk are clamped to
-    // it (fetched, never used).
+    // and are rebuilt in iteration j + 1 (kRegW: three sets, see the K loop).
+    // Requests past the last chunk are clamped to it (fetched, never used).
     int woff[TPW], woff_half[TPW], poff[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
@@ -686,11 +696,23 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
         poff[i] = tr * ptile + (WF == kW4Lqq ? (c & ~1) * 2 : (c & ~3));
     }
     const WParamSel psel = wparam_selectors<WF>(c);
-    WRec<WF> wrec0[TPW], wrec1[TPW];
-    uint32_t wsc0[TPW][2], wsc1[TPW][2];
+    WRec<WF> wrec0[TPW], wrec1[TPW], wrec2[TPW];
+    uint32_t wsc0[TPW][2], wsc1[TPW][2], wsc2[TPW][2];
+    auto wrec_of = [&](auto st) -> WRec<WF>(&)[TPW] {
+        constexpr int S = (int)decltype(st)::value;
+        if constexpr (S == 0) return wrec0;
+        else if constexpr (S == 1) return wrec1;
+        else return wrec2;
+    };
+    auto wsc_of = [&](auto st) -> uint32_t(&)[TPW][2] {
+        constexpr int S = (int)decltype(st)::value;
+        if constexpr (S == 0) return wsc0;
+        else if constexpr (S == 1) return wsc1;
+        else return wsc2;
+    };
     auto fetch_w = [&](int jreq, auto set_tag) {
-        WRec<WF>(&wrec)[TPW] = decltype(set_tag)::value ? wrec1 : wrec0;
-        uint32_t(&wsc)[TPW][2] = decltype(set_tag)::value ? wsc1 : wsc0;
+        WRec<WF>(&wrec)[TPW] = wrec_of(set_tag);
+        uint32_t(&wsc)[TPW][2] = wsc_of(set_tag);
         const int j = jreq < nchunks ? jreq : nchunks - 1;
         const bool wfull = j < nfull;
 #pragma unroll
@@ -712,7 +734,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     // of the 16-byte window (see above) into the step-0 words.
     auto half_records = [&](auto set_tag) {
         if constexpr (WF != kW8) {
-            WRec<WF>(&wrec)[TPW] = decltype(set_tag)::value ? wrec1 : wrec0;
+            WRec<WF>(&wrec)[TPW] = wrec_of(set_tag);
 #pragma unroll
             for (int i = 0; i < TPW; ++i)
                 wrec[i].r = (lane == 63) ? u32x4{wrec[i].r.z, wrec[i].r.w, 0u, 0u}
@@ -773,15 +795,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     // 4 h + kq; weight fragments are stored in operand order.
     const int kq = lane >> 4;
     auto mma_step = [&](auto buf_tag, int h) {
-        const uint8_t *abase = decltype(buf_tag)::value ? act1 : act0;
+        const uint8_t *abase = act_of(buf_tag);
         const uint8_t *wbase = decltype(buf_tag)::value ? wl1 : wl0;
         v4i av[TM], wv[TN];
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm)
             av[tm] = *(const v4i *)(abase + act_lds_off(wm * WM + tm * 16 + c, 4 * h + kq));
         if constexpr (kRegW) {
-            const WRec<WF>(&wrec)[TPW] = decltype(buf_tag)::value ? wrec1 : wrec0;
-            const uint32_t(&wsc)[TPW][2] = decltype(buf_tag)::value ? wsc1 : wsc0;
+            const WRec<WF>(&wrec)[TPW] = wrec_of(buf_tag);
+            const uint32_t(&wsc)[TPW][2] = wsc_of(buf_tag);
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn) {
                 uint32_t mul = 0u, add = 0u;
@@ -858,19 +880,44 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     // rebuild's VALU work.
     const std::integral_constant<bool, false> stage0;
     const std::integral_constant<bool, true> stage1;
-    if (nchunks > 0) {
-        fetch_w(0, stage0);
-        if constexpr (!kRegW) fetch_w(1, stage1);
-        if (nfull > 0) {
-            if constexpr (!kRegW) rebuild_w(stage0, full_chunk);
-            issue_act(0, stage0, full_chunk);
-        } else {
-            if constexpr (!kRegW) rebuild_w(stage0, half_chunk);
-            issue_act(0, stage0, half_chunk);
+    // kRegW: vector-memory requests one chunk makes (activation blocks, then
+    // per tile a record and two parameter words, or two int8 records).  The
+    // barrier waits until at most that many remain: loads complete in order,
+    // so that is exactly the older chunk, and the newer one stays in flight.
+    constexpr int kChunkReq = ACT_I + TPW * (WF == kW8 ? 2 : 3);
+    static_assert(!kRegW || (AB == 0 && kChunkReq < 64), "one chunk of requests in flight");
+    constexpr int kWaitOlder = (kChunkReq & 15) | ((kChunkReq >> 4) << 14) | 0x70;  // lgkmcnt 0
+    const std::integral_constant<int, 2> stage2;
+    if constexpr (kRegW) {
+        if (nchunks > 0) {
+            if (nfull > 0) issue_act(0, stage0, full_chunk);
+            else issue_act(0, stage0, half_chunk);
+            fetch_w(0, stage0);
+            // chunk 1, or chunk 0 again when there is no chunk 1 (never used)
+            const int j1 = nchunks > 1 ? 1 : 0;
+            if (j1 < nfull) issue_act(j1, stage1, full_chunk);
+            else issue_act(j1, stage1, half_chunk);
+            fetch_w(1, stage1);
         }
-        if constexpr (AB > 0) fetch_s(0, scur);
+        __builtin_amdgcn_s_waitcnt(kWaitOlder);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    } else {
+        if (nchunks > 0) {
+            fetch_w(0, stage0);
+            fetch_w(1, stage1);
+            if (nfull > 0) {
+                rebuild_w(stage0, full_chunk);
+                issue_act(0, stage0, full_chunk);
+            } else {
+                rebuild_w(stage0, half_chunk);
+                issue_act(0, stage0, half_chunk);
+            }
+            if constexpr (AB > 0) fetch_s(0, scur);
+        }
+        W4A8_LDS_BARRIER();
     }
-    W4A8_LDS_BARRIER();
     auto iteration = [&](int j, auto cur, auto nxt) {
         if (j + 1 < nfull) issue_act(j + 1, nxt, full_chunk);
         else if (j + 1 < nchunks) issue_act(j + 1, nxt, half_chunk);
@@ -896,21 +943,35 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     // chunk j + 1 (into the other stage and register set), then multiplies
     // chunk j with its operands rebuilt in registers from the records of its
     // set, which the previous barrier's wait covered.
-    auto iteration_rw = [&](int j, auto cur, auto nxt) {
-        if (j + 1 < nfull) issue_act(j + 1, nxt, full_chunk);
-        else if (j + 1 < nchunks) issue_act(j + 1, nxt, half_chunk);
-        fetch_w(j + 1, nxt);
+    // kRegW: three stages, two chunks ahead.  Iteration j requests the
+    // activations and weight records of chunk j + 2 into the stage and
+    // register set that chunk j - 1 used, multiplies chunk j with its
+    // operands rebuilt in registers from the records of its set, and ends on
+    // a barrier that waits for chunk j + 1's requests only.  Requests past
+    // the last chunk are clamped to it (every address stays inside the
+    // operands) and land in a stage and set that are not used again.
+    auto iteration_rw = [&](int j, auto cur, auto ahead) {
+        const int ja = j + 2 < nchunks ? j + 2 : nchunks - 1;
+        if (ja < nfull) issue_act(ja, ahead, full_chunk);
+        else issue_act(ja, ahead, half_chunk);
+        fetch_w(j + 2, ahead);
         __builtin_amdgcn_sched_barrier(0);
         if (j >= nfull) half_records(cur);
         mma_step(cur, 0);
         if (j < nfull) mma_step(cur, 1);
-        W4A8_LDS_BARRIER();
+        __builtin_amdgcn_s_waitcnt(kWaitOlder);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
     };
-    for (int j = 0; j < nchunks; j += 2) {
-        if constexpr (kRegW) {
-            iteration_rw(j, stage0, stage1);
+    if constexpr (kRegW) {
+        for (int j = 0; j < nchunks; j += 3) {
+            iteration_rw(j, stage0, stage2);
             if (j + 1 < nchunks) iteration_rw(j + 1, stage1, stage0);
-        } else {
+            if (j + 2 < nchunks) iteration_rw(j + 2, stage2, stage1);
+        }
+    } else {
+        for (int j = 0; j < nchunks; j += 2) {
             iteration(j, stage0, stage1);
             if (j + 1 < nchunks) iteration(j + 1, stage1, stage0);
         }
@@ -936,7 +997,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
         const int segs = row_bytes / 16;                 // 16-byte segments per row
         // kRegW: the weight stages held no operands; half the wavefronts use each
         constexpr int PER_W = WAVES / 2;
-        static_assert(kRegW ? WM * WN * 2 * PER_W <= L::kW
+        static_assert(kRegW ? WM * WN * 2 * PER_W <= kEpiW
                             : WM * WN * 2 <= (L::kW < L::kAct ? L::kW : L::kAct) / PER_ARRAY,
                       "epilogue tile fits the stage arrays");
         const int which = wave / PER_ARRAY;
