@@ -141,6 +141,7 @@ GEMM_SHAPES = [
     (129, 144, 4160),   # K = 32.5 chunks
     (37, 8192, 1088),   # skinny path with row splits (>= 512 tiles), ragged M, half chunk
     (64, 8208, 640),    # row splits, odd tile count (last workgroup half empty)
+    (4000, 4368, 192),  # 256 large tiles, then a 128 x 256 tail launch; ragged M and N in both
 ]
 
 
@@ -230,7 +231,8 @@ def test_fused_splitk_workspace_equals_without(w4a8, fmt):
 
 
 @pytest.mark.parametrize("m,n,k", [(16, 256, 256), (5, 48, 192), (65, 48, 192),
-                                   (200, 272, 384), (8, 4096, 4096), (50, 8192, 576)])
+                                   (200, 272, 384), (8, 4096, 4096), (50, 8192, 576),
+                                   (4000, 4368, 192)])
 def test_gemm_float_outputs(w4a8, m, n, k):
     announce("gemm f32/bf16", m, n, k)
     _, dev_w, ref_w = _pack(w4a8, n, k, seed=3 * m + n)

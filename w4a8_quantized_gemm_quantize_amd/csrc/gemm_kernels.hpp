@@ -1262,7 +1262,9 @@ void launch_tiled_large(const int8_t *a_q, const float *a_scale, const uint8_t *
     const int64_t n_large = best_cols * 256 < n ? best_cols * 256 : n;
     launch_tiled_cols<WF, 256, 256, 4, 4>(a_q, a_scale, w_packed, grp_scale, ch_scale, m, 0,
                                           n_large, n, k, out, out_dtype, stream);
-    launch_tiled_cols<WF, 128, 256, 2, 4>(a_q, a_scale, w_packed, grp_scale, ch_scale, m,
+    // the tail as one row of 8 wavefronts of 128 x 32: weights unpacked in
+    // registers (half the LDS writes of a 2 x 4 layout with LDS weights)
+    launch_tiled_cols<WF, 128, 256, 1, 8>(a_q, a_scale, w_packed, grp_scale, ch_scale, m,
                                           n_large, n - n_large, n, k, out, out_dtype, stream);
 }
 
