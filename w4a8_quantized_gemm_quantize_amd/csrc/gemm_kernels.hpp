@@ -893,6 +893,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
             if (nfull > 0) issue_act(0, stage0, full_chunk);
             else issue_act(0, stage0, half_chunk);
             fetch_w(0, stage0);
+            // every request of chunk 0 before any of chunk 1: the wait below
+            // counts on that order
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("" ::: "memory");
             // chunk 1, or chunk 0 again when there is no chunk 1 (never used)
             const int j1 = nchunks > 1 ? 1 : 0;
             if (j1 < nfull) issue_act(j1, stage1, full_chunk);
