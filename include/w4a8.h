@@ -168,8 +168,11 @@ w4a8_status w4a8_gemm(const int8_t *a_q, const float *a_scale, const uint8_t *w_
  * Bytes of optional scratch that lets w4a8_gemm_ws (and the fused entry points
  * below) split K over workgroups for an m x n x k product: int32 partial sums,
  * for 16 < m <= 64 (decode-batch shapes whose one-pass kernel re-reads all of
- * A in every workgroup).  0 when that shape is not split.  Part of the GEMM
- * design choices, not of the method: the result is the same bit for bit.
+ * A in every workgroup).  0 when that shape is not split: m outside that
+ * range, fewer than two 128-wide chunks of K, or K too short for the partials
+ * (S slices of m * n int32, S up to 16) to stay within half the weight bytes
+ * (32 * S * m > k).  Part of the GEMM design choices, not of the method: the
+ * result is the same bit for bit.
  */
 size_t w4a8_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
