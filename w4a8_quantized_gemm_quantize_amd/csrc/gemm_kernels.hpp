@@ -533,6 +533,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 // into the other stage.  The MFMA loop itself is LDS reads and MFMAs only, and
 // small per-wavefront register budgets keep four wavefronts per SIMD so the
 // matrix cores always have work to issue.
+// With one row of wavefronts (WAVES_M == 1) each wavefront multiplies only the
+// tiles it fetches, so the weight stage is skipped: operands are rebuilt in
+// registers right before their MFMAs, and three activation stages keep two
+// chunks of loads in flight (the split-K tile and the tail launch).
 template <int BM, int BN>
 struct TiledLds {
     static constexpr int kAct = BM * kChunkK;                 // activations
@@ -943,10 +947,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
                 for (int b = 0; b < NBC; ++b) scur[tm][b] = snxt[tm][b];
         }
     };
-    // kRegW: iteration j requests the activations and the weight records of
-    // chunk j + 1 (into the other stage and register set), then multiplies
-    // chunk j with its operands rebuilt in registers from the records of its
-    // set, which the previous barrier's wait covered.
     // kRegW: three stages, two chunks ahead.  Iteration j requests the
     // activations and weight records of chunk j + 2 into the stage and
     // register set that chunk j - 1 used, multiplies chunk j with its
