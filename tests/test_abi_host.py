@@ -10,6 +10,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -179,6 +180,14 @@ def test_gemm_ws_workspace_and_validation(lib):
     assert ws(17, 256, 10304) == 17 * 17 * 256 * 4        # 16 x 5 chunks + a half-chunk slice
     assert ws(48, 8192, 8192) == 0                        # partials would outweigh the gain
     assert ws(64, 8192, 4096) == 0
+    # the rule over seeded random shapes around its edges (m range, half chunks,
+    # the 16-slice cap, the 32 S m <= k cut)
+    rng = np.random.default_rng(7)
+    for _ in range(2000):
+        m = int(rng.integers(0, 80))
+        n = 16 * int(rng.integers(1, 2400))
+        k = 64 * int(rng.integers(1, 600))
+        assert ws(m, n, k) == splitk_bytes_expected(m, n, k), (m, n, k)
     g = lib.w4a8_gemm_ws
     g.argtypes = [P, P, P, P, P, I64, I64, I64, I32, P, ctypes.c_int, P, ctypes.c_size_t, P]
     need = ws(64, 8192, 28672)
