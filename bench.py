@@ -73,6 +73,26 @@ def quantizer_algorithmic_bytes(elems, block):
     return elems * 3 + 4 * (elems // block)
 
 
+def copy_probe_gbps(torch, dev, reps=10):
+    """Measured HBM reference: a 256 MiB device-to-device copy (bytes read +
+    bytes written per second), timed with HIP events after a warmup."""
+    x = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * 4 * x.numel() * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x, y
+    return gbps
+
+
 def time_graph(torch, fn, copies, reps):
     """Capture fn(r, stream) for r in range(copies) into one HIP graph, replay it
     once untimed, then `reps` times between HIP events on the capture stream.
@@ -279,6 +299,10 @@ def main():
         achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBPS}
+        # the same against a measured reference on this GPU
+        probe = copy_probe_gbps(torch, dev)
+        roof["probe"] = {"kind": "256 MiB device copy, read + written", "achieved": probe,
+                         "unit": "GB/s", "frac_of_probe": achieved / probe}
     else:
         achieved = ops / (gemm_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
