@@ -187,6 +187,36 @@ def test_w8a8_float_outputs_and_fused(w4a8, m, n, k):
     assert torch.equal(yf.view(torch.int32), y32.view(torch.int32))
 
 
+# ------------------------------------------------- split K, LQQ and W8A8 --
+
+@pytest.mark.parametrize("fmt", ["lqq", "w8"])
+@pytest.mark.parametrize("m,n,k", [(24, 14352, 4096),   # ragged N, 5 slices
+                                   (33, 8208, 8448)])   # ragged M, on the split threshold
+def test_fused_split_k_matches_oracle(w4a8, fmt, m, n, k):
+    """With room for the partials the fused calls split K: their int32 sums are
+    the oracle's exactly and their fp32 outputs within the fp32 bar."""
+    announce("fused split-K vs oracle", fmt, m, n, k)
+    assert w4a8.gemm_workspace_bytes(m, n, k) > 0
+    a = inputs.activations(m, k, seed=m + 7, outlier_frac=0.001)
+    a_q, a_s = oracle.quantize_act_blockwise(a, k)
+    if fmt == "lqq":
+        dev_w, ref_w = _lqq_pack(w4a8, n, k, seed=n + 11)
+        fn = w4a8.w4a8_gemm_lqq_bf16act
+        acc_ref, y_ref = oracle.w4a8_gemm_lqq(a_q, a_s, *ref_w, 64)
+    else:
+        w = edge_weights(n, k, seed=n + 13)
+        dev_w = w4a8.pack_w8_channel(to_dev_bf16(w))
+        fn = w4a8.w8a8_gemm_bf16act
+        acc_ref, y_ref = oracle.w8a8_gemm(a_q, a_s, *oracle.quantize_w8_channel(w))
+    ws = torch.empty(w4a8.workspace_bytes(m, k, n), dtype=torch.uint8, device="cuda")
+    a_d = to_dev_bf16(a)
+    acc = fn(a_d, *dev_w, n, out_dtype=torch.int32, workspace=ws)
+    y32 = fn(a_d, *dev_w, n, out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    assert_f32_close(y32.cpu().numpy(), y_ref)
+
+
 # ------------------------------------------------------ EQuARX receive step --
 
 @pytest.mark.parametrize("rows,cols,block,xtype,want_sum", [
