@@ -592,6 +592,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     __shared__ __attribute__((aligned(16))) uint8_t act2[kRegW ? L::kAct : 16];
     __shared__ __attribute__((aligned(16))) uint8_t wl0[kRegW ? kEpiW : L::kW];
     __shared__ __attribute__((aligned(16))) uint8_t wl1[kRegW ? kEpiW : L::kW];
+    // Per-token scales of the tile's rows and channel scales of its columns,
+    // whole 1 KB blocks for the direct-to-LDS loads (per-token scales only).
+    constexpr bool kSclLds = AB == 0;
+    constexpr int kSclA = (BM * 4 + 1023) / 1024, kSclC = (BN * 4 + 1023) / 1024;
+    __shared__ __attribute__((aligned(16))) uint8_t scl_a[kSclLds ? kSclA * 1024 : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t scl_c[kSclLds ? kSclC * 1024 : 16];
 
     const int tid = threadIdx.x;
     // readfirstlane: the compiler then knows the wavefront index is uniform,
@@ -651,6 +657,25 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
         buffer_rsrc(w_packed + t0 * (int64_t)wtile, (uint32_t)tiles_here * wtile);
     const __amdgpu_buffer_rsrc_t rp =
         WF == kW8 ? rw : buffer_rsrc(grp_scale + t0 * (int64_t)ptile, (uint32_t)tiles_here * ptile);
+
+    // The epilogue's scales go to LDS before any chunk is requested, so they
+    // are in long before the K loop ends; read from global memory at the
+    // epilogue they would queue behind the output stores of every other
+    // workgroup finishing the same round.  Rows past m and columns past n read
+    // zero and are not stored.  These are the oldest loads of the wavefronts
+    // that issue them, so every wait below covers them.
+    if constexpr (kSclLds) {
+        static_assert(WAVES >= kSclA + kSclC, "one scale block per wavefront");
+        if (wave < kSclA) {
+            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a_scale + m0, (uint32_t)rows_here * 4);
+            buffer_to_lds16(rs, scl_a + wave * 1024, wave * 1024 + lane * 16, 0);
+        } else if (wave < kSclA + kSclC) {
+            const int b = wave - kSclA;
+            const int cols_here = (int)(n - n0 < BN ? n - n0 : BN);
+            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(ch_scale + n0, (uint32_t)cols_here * 4);
+            buffer_to_lds16(rs, scl_c + b * 1024, b * 1024 + lane * 16, 0);
+        }
+    }
 
     // Activations of chunk j -> stage buf, buffer -> LDS directly (one 1 KB
     // block = 8 rows of 128 bytes per instruction, 16-byte columns swizzled).
@@ -1014,13 +1039,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
         auto seg_off = [&](int r, int seg) {
             return r * row_bytes + ((seg ^ (r & swz_mask)) << 4);
         };
-        // channel scales of this lane's 4 columns per 16-column tile (clamped
-        // past n: those columns are not stored)
+        // channel scales of this lane's 4 columns per 16-column tile (past n:
+        // zero or clamped; those columns are not stored)
         f32x4 scv[TN];
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
-            const int64_t nn = n0 + wn * WN + tn * 16 + 4 * kq;
-            scv[tn] = *(const f32x4 *)(ch_scale + (nn < n ? nn : n - 4));
+            const int col = wn * WN + tn * 16 + 4 * kq;
+            if constexpr (kSclLds) {
+                scv[tn] = *(const f32x4 *)(scl_c + col * 4);
+            } else {
+                const int64_t nn = n0 + col;
+                scv[tn] = *(const f32x4 *)(ch_scale + (nn < n ? nn : n - 4));
+            }
         }
         for (int pass = 0; pass < WM / rows_pass; ++pass) {
             // accumulators -> LDS (lane (c, kq): row tm * 16 + c, 4 columns)
@@ -1028,8 +1058,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
             for (int tm = 0; tm < TM; ++tm) {
                 const int r = tm * 16 + c - pass * rows_pass;
                 if (r < 0 || r >= rows_pass) continue;
-                const int64_t row = m0 + wm * WM + tm * 16 + c;
-                const float sa = AB ? 1.0f : a_scale[row < m ? row : m - 1];
+                const float sa =
+                    AB ? 1.0f : *(const float *)(scl_a + (wm * WM + tm * 16 + c) * 4);
 #pragma unroll
                 for (int tn = 0; tn < TN; ++tn) {
                     const int col = tn * 16 + 4 * kq;             // within the wavefront tile
