@@ -337,6 +337,43 @@ def test_empty_and_degenerate_shapes(w4a8):
         w4a8.quantize_act_blockwise(torch.zeros((2, 48), dtype=torch.bfloat16, device=dev), 32)
 
 
+def test_binding_rejects_undersized_buffers(w4a8):
+    """The library sees raw pointers only; the binding checks every tensor
+    against the call's sizes and raises before launching."""
+    announce("binding size checks")
+    dev = "cuda"
+    m, n, k = 8, 64, 256
+    _, (wp, gs, cs), _ = _pack(w4a8, n, k, seed=4)
+    a_q = torch.zeros((m, k), dtype=torch.int8, device=dev)
+    a_s = torch.ones(m, dtype=torch.float32, device=dev)
+    cases = [
+        dict(out=torch.empty((m, n - 16), dtype=torch.float32, device=dev)),
+        dict(w_packed=wp[: wp.numel() - 16]),
+        dict(grp_scale=gs[:-1]),
+        dict(ch_scale=cs[: n - 4]),
+        dict(a_scale=a_s[: m - 1]),
+    ]
+    for over in cases:
+        args = dict(a_q=a_q, a_scale=a_s, w_packed=wp, grp_scale=gs, ch_scale=cs)
+        out = over.pop("out", None)
+        args.update(over)
+        with pytest.raises(w4a8.W4A8SizeError):
+            w4a8.w4a8_gemm(args["a_q"], args["a_scale"], args["w_packed"], args["grp_scale"],
+                           args["ch_scale"], n, out=out, out_dtype=torch.float32)
+    with pytest.raises(ValueError):            # group scales given as floats
+        w4a8.w4a8_gemm(a_q, a_s, wp, gs.float(), cs, n)
+    with pytest.raises(ValueError):            # a strided output view
+        w4a8.w4a8_gemm(a_q, a_s, wp, gs, cs, n,
+                       out=torch.empty((m, 2 * n), dtype=torch.float32, device=dev)[:, ::2])
+    with pytest.raises(w4a8.W4A8SizeError):    # fused call, output too small
+        w4a8.w4a8_gemm_bf16act(torch.zeros((m, k), dtype=torch.bfloat16, device=dev), wp, gs, cs,
+                               n, out=torch.empty((m * n - 1,), dtype=torch.bfloat16, device=dev))
+    # the right sizes still run
+    y = w4a8.w4a8_gemm(a_q, a_s, wp, gs, cs, n, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert (y == 0).all()
+
+
 def test_determinism(w4a8):
     m, n, k = 300, 256, 2048
     announce("determinism", m, n, k)

@@ -111,6 +111,52 @@ def _dev(t, dtype, name):
         raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor")
 
 
+class W4A8SizeError(W4A8Error):
+    """A tensor argument holds fewer elements than the call's sizes need (raised
+    before anything is launched; status W4A8_ERR_SHAPE)."""
+
+    def __init__(self, fn: str, name: str, have: int, need: int):
+        self.status = ERR_SHAPE
+        RuntimeError.__init__(self, f"{fn}: {name} holds {have} elements, the call needs {need}")
+
+
+_U8 = (torch.uint8, torch.int8)
+_I16 = (torch.int16,)
+_F32 = (torch.float32,)
+
+
+def _sized(fn, t, dtypes, need, name):
+    """The library takes raw pointers and cannot see buffer sizes: check that a
+    tensor argument is a contiguous CUDA tensor of one of `dtypes` holding at
+    least `need` elements.  None passes through (the library rejects a missing
+    pointer itself)."""
+    if t is None:
+        return
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous()):
+        raise ValueError(f"{fn}: {name} must be a contiguous CUDA tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{fn}: {name} must be of dtype {' or '.join(map(str, dtypes))}, "
+                         f"not {t.dtype}")
+    if t.numel() < need:
+        raise W4A8SizeError(fn, name, t.numel(), need)
+
+
+def _per(total: int, block: int) -> int:
+    return total // block if block > 0 else 0
+
+
+def _gemm_args(fn, m, n, k, a_scale, w_packed, w_bytes_per_elem, params, param_dtypes,
+               group, ch_scale, out):
+    """Sizes of the GEMM operands: a_scale [m], weights n k w_bytes_per_elem bytes,
+    group parameters [n, k / group] (if the format has them), ch_scale [n], out [m, n]."""
+    _sized(fn, a_scale, _F32, m, "a_scale")
+    _sized(fn, w_packed, _U8, (n * k * w_bytes_per_elem) // 2, "w_packed")
+    if param_dtypes is not None:
+        _sized(fn, params, param_dtypes, n * _per(k, group), "group parameters")
+    _sized(fn, ch_scale, _F32, n, "ch_scale")
+    _sized(fn, out, tuple(_OUT), m * n, "out")
+
+
 # ------------------------------------------------------------ activations --
 
 def quantize_act_blockwise(x: torch.Tensor, block: int, q=None, scales=None, stream=None):
@@ -122,6 +168,8 @@ def quantize_act_blockwise(x: torch.Tensor, block: int, q=None, scales=None, str
     if scales is None:
         scales = torch.empty((rows, cols // block if block > 0 else 0), dtype=torch.float32,
                              device=x.device)
+    _sized("quantize_act_blockwise", q, (torch.int8,), rows * cols, "q")
+    _sized("quantize_act_blockwise", scales, _F32, rows * _per(cols, block), "scales")
     _check("quantize_act_blockwise",
            _lib.quantize_act_blockwise(_ptr(x), rows, cols, block, _ptr(q), _ptr(scales),
                                        _stream(stream)))
@@ -137,6 +185,8 @@ def dequantize_act_blockwise(q: torch.Tensor, scales: torch.Tensor, block: int,
     code = {torch.float32: F32, torch.bfloat16: BF16}[out_dtype]
     if out is None:
         out = torch.empty((rows, cols), dtype=out_dtype, device=q.device)
+    _sized("dequantize_act_blockwise", scales, _F32, rows * _per(cols, block), "scales")
+    _sized("dequantize_act_blockwise", out, (out_dtype,), rows * cols, "out")
     _check("dequantize_act_blockwise",
            _lib.dequantize_act_blockwise(_ptr(q), _ptr(scales), rows, cols, block, _ptr(out),
                                          code, _stream(stream)))
@@ -165,6 +215,8 @@ def unpack_w4_grouped(w_packed, grp_scale, n: int, k: int, group: int = GROUP, s
     dev = w_packed.device
     q = torch.empty((n, k), dtype=torch.int8, device=dev)
     s_g = torch.empty((n, k // group), dtype=torch.uint8, device=dev)
+    _sized("unpack_w4_grouped", w_packed, _U8, n * k // 2, "w_packed")
+    _sized("unpack_w4_grouped", grp_scale, _U8, n * _per(k, group), "grp_scale")
     _check("unpack_w4_grouped",
            _lib.unpack_w4_grouped(_ptr(w_packed), _ptr(grp_scale), n, k, group, _ptr(q),
                                   _ptr(s_g), _stream(stream)))
@@ -183,6 +235,7 @@ def w4a8_gemm(a_q, a_scale, w_packed, grp_scale, ch_scale, n: int, out_dtype=tor
     m, k = a_q.shape
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=a_q.device)
+    _gemm_args("w4a8_gemm", m, n, k, a_scale, w_packed, 1, grp_scale, _U8, group, ch_scale, out)
     _check("w4a8_gemm",
            _lib.w4a8_gemm(_ptr(a_q), _ptr(a_scale), _ptr(w_packed), _ptr(grp_scale),
                           _ptr(ch_scale), m, n, k, group, _ptr(out), _OUT[out.dtype],
@@ -206,6 +259,9 @@ def w4a8_gemm_ws(a_q, a_scale, w_packed, grp_scale, ch_scale, n: int,
     need = gemm_workspace_bytes(m, n, k)
     if workspace is None and need > 0:
         workspace = torch.empty((need,), dtype=torch.uint8, device=a_q.device)
+    _gemm_args("w4a8_gemm_ws", m, n, k, a_scale, w_packed, 1, grp_scale, _U8, group, ch_scale,
+               out)
+    _sized("w4a8_gemm_ws", workspace, _U8, 0, "workspace")
     _check("w4a8_gemm_ws",
            _lib.w4a8_gemm_ws(_ptr(a_q), _ptr(a_scale), _ptr(w_packed), _ptr(grp_scale),
                              _ptr(ch_scale), m, n, k, group, _ptr(out), _OUT[out.dtype],
@@ -231,6 +287,9 @@ def w4a8_gemm_bf16act(a, w_packed, grp_scale, ch_scale, n: int, out_dtype=torch.
     need = workspace_bytes(m, k, n)
     if workspace is None:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=a.device)
+    _gemm_args("w4a8_gemm_bf16act", m, n, k, None, w_packed, 1, grp_scale, _U8, group, ch_scale,
+               out)
+    _sized("w4a8_gemm_bf16act", workspace, _U8, 0, "workspace")
     _check("w4a8_gemm_bf16act",
            _lib.w4a8_gemm_bf16act(_ptr(a), _ptr(w_packed), _ptr(grp_scale), _ptr(ch_scale), m,
                                   n, k, group, _ptr(out), _OUT[out.dtype], _ptr(workspace),
@@ -270,6 +329,8 @@ def unpack_w4_lqq(w_packed, grp_param, n: int, k: int, group: int = GROUP, strea
     q = torch.empty((n, k), dtype=torch.uint8, device=dev)
     s_u8 = torch.empty((n, k // group), dtype=torch.uint8, device=dev)
     w_min = torch.empty((n, k // group), dtype=torch.int8, device=dev)
+    _sized("unpack_w4_lqq", w_packed, _U8, n * k // 2, "w_packed")
+    _sized("unpack_w4_lqq", grp_param, _I16, n * _per(k, group), "grp_param")
     _check("unpack_w4_lqq",
            _lib.unpack_w4_lqq(_ptr(w_packed), _ptr(grp_param), n, k, group, _ptr(q),
                               _ptr(s_u8), _ptr(w_min), _stream(stream)))
@@ -282,6 +343,8 @@ def w4a8_gemm_lqq(a_q, a_scale, w_packed, grp_param, ch_scale, n: int,
     m, k = a_q.shape
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=a_q.device)
+    _gemm_args("w4a8_gemm_lqq", m, n, k, a_scale, w_packed, 1, grp_param, _I16, group,
+               ch_scale, out)
     _check("w4a8_gemm_lqq",
            _lib.w4a8_gemm_lqq(_ptr(a_q), _ptr(a_scale), _ptr(w_packed), _ptr(grp_param),
                               _ptr(ch_scale), m, n, k, group, _ptr(out), _OUT[out.dtype],
@@ -298,6 +361,9 @@ def w4a8_gemm_lqq_bf16act(a, w_packed, grp_param, ch_scale, n: int, out_dtype=to
     if workspace is None:
         workspace = torch.empty((max(workspace_bytes(m, k, n), 16),), dtype=torch.uint8,
                                 device=a.device)
+    _gemm_args("w4a8_gemm_lqq_bf16act", m, n, k, None, w_packed, 1, grp_param, _I16, group,
+               ch_scale, out)
+    _sized("w4a8_gemm_lqq_bf16act", workspace, _U8, 0, "workspace")
     _check("w4a8_gemm_lqq_bf16act",
            _lib.w4a8_gemm_lqq_bf16act(_ptr(a), _ptr(w_packed), _ptr(grp_param), _ptr(ch_scale),
                                       m, n, k, group, _ptr(out), _OUT[out.dtype],
@@ -320,6 +386,7 @@ def pack_w8_channel(w: torch.Tensor, stream=None):
 
 def unpack_w8_channel(w_packed, n: int, k: int, stream=None):
     q8 = torch.empty((n, k), dtype=torch.int8, device=w_packed.device)
+    _sized("unpack_w8_channel", w_packed, _U8, n * k, "w_packed")
     _check("unpack_w8_channel",
            _lib.unpack_w8_channel(_ptr(w_packed), n, k, _ptr(q8), _stream(stream)))
     return q8
@@ -331,6 +398,7 @@ def w8a8_gemm(a_q, a_scale, w_packed, ch_scale, n: int, out_dtype=torch.bfloat16
     m, k = a_q.shape
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=a_q.device)
+    _gemm_args("w8a8_gemm", m, n, k, a_scale, w_packed, 2, None, None, GROUP, ch_scale, out)
     _check("w8a8_gemm",
            _lib.w8a8_gemm(_ptr(a_q), _ptr(a_scale), _ptr(w_packed), _ptr(ch_scale), m, n, k,
                           _ptr(out), _OUT[out.dtype], _stream(stream)))
@@ -346,6 +414,8 @@ def w8a8_gemm_bf16act(a, w_packed, ch_scale, n: int, out_dtype=torch.bfloat16, o
     if workspace is None:
         workspace = torch.empty((max(workspace_bytes(m, k, n), 16),), dtype=torch.uint8,
                                 device=a.device)
+    _gemm_args("w8a8_gemm_bf16act", m, n, k, None, w_packed, 2, None, None, GROUP, ch_scale, out)
+    _sized("w8a8_gemm_bf16act", workspace, _U8, 0, "workspace")
     _check("w8a8_gemm_bf16act",
            _lib.w8a8_gemm_bf16act(_ptr(a), _ptr(w_packed), _ptr(ch_scale), m, n, k, _ptr(out),
                                   _OUT[out.dtype], _ptr(workspace), workspace.numel(),
@@ -363,6 +433,10 @@ def w4a8_gemm_blockact(a_q, a_scale, w_packed, grp_scale, ch_scale, n: int, bloc
     m, k = a_q.shape
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=a_q.device)
+    _gemm_args("w4a8_gemm_blockact", 0, n, k, None, w_packed, 1, grp_scale, _U8, group,
+               ch_scale, out)
+    _sized("w4a8_gemm_blockact", a_scale, _F32, m * _per(k, block), "a_scale")
+    _sized("w4a8_gemm_blockact", out, tuple(_OUT), m * n, "out")
     _check("w4a8_gemm_blockact",
            _lib.w4a8_gemm_blockact(_ptr(a_q), _ptr(a_scale), _ptr(w_packed), _ptr(grp_scale),
                                    _ptr(ch_scale), m, n, k, group, block, _ptr(out),
@@ -390,6 +464,12 @@ def dequant_add_requant(q_in, s_in, x, block: int, want_sum: bool = False, q_out
                             device=dev)
     if want_sum and sum_out is None:
         sum_out = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+    fn = "dequant_add_requant"
+    _sized(fn, s_in, _F32, rows * _per(cols, block), "s_in")
+    _sized(fn, x, (x.dtype,), rows * cols, "x")
+    _sized(fn, q_out, (torch.int8,), rows * cols, "q_out")
+    _sized(fn, s_out, _F32, rows * _per(cols, block), "s_out")
+    _sized(fn, sum_out, _F32, rows * cols, "sum_out")
     _check("dequant_add_requant",
            _lib.dequant_add_requant(_ptr(q_in), _ptr(s_in), _ptr(x),
                                     BF16 if x.dtype == torch.bfloat16 else F32, rows, cols,
