@@ -255,9 +255,11 @@ def main():
 
     # One eager step per weight copy on a side stream, then capture `copies`
     # steps (one per weight copy) into one HIP graph; the rest of the warmup
-    # and the timed region replay it.  Under sustained load the first few
-    # hundred steps run slower (clocks settle), so the warmup is in steps of
-    # the graph itself.
+    # and the timed region replay it, with a graph of the first K mod copies
+    # steps for a remainder, so exactly W steps run untimed (at least the
+    # `copies` eager ones) and exactly K are timed.  Under sustained load the
+    # first few hundred steps run slower (clocks settle), so the warmup is in
+    # steps of the graph itself.
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -266,28 +268,34 @@ def main():
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
 
-    def capture(fn):
+    def capture(fn, count=copies):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             s = torch.cuda.current_stream()
-            for r in range(copies):
+            for r in range(count):
                 fn(r, s)
         return g
 
+    def run_steps(count):
+        """Replay exactly `count` steps: whole graphs of `copies` steps, then a
+        graph of the first count % copies steps (captured beforehand)."""
+        for _ in range(count // copies):
+            g_step.replay()
+        if count % copies:
+            partial[count % copies].replay()
+
     g_step = capture(step)
-    reps = max(1, (args.steps + copies - 1) // copies)
-    steps = reps * copies
+    steps = max(1, args.steps)
+    warm_graph = max(0, args.warmup - copies)   # the eager priming ran `copies` steps
+    partial = {r: capture(step, r) for r in {steps % copies, warm_graph % copies} if r}
     stream = torch.cuda.current_stream()
-    warm_reps = max(1, (args.warmup - 1) // copies)   # (W - copies) / copies, rounded up
-    for _ in range(warm_reps):
-        g_step.replay()
+    run_steps(warm_graph)
     torch.cuda.synchronize()
-    warmup_steps = copies + warm_reps * copies        # untimed steps actually run
+    warmup_steps = max(args.warmup, copies)           # untimed steps actually run
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
-    for _ in range(reps):
-        g_step.replay()
+    run_steps(steps)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / steps
@@ -305,12 +313,13 @@ def main():
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        reps = max(1, steps // copies)
         e0.record(stream)
         for _ in range(reps):
             g_gemm.replay()
         e1.record(stream)
         torch.cuda.synchronize()
-        gemm_ms = e0.elapsed_time(e1) / steps
+        gemm_ms = e0.elapsed_time(e1) / (reps * copies)
 
     ops = 2.0 * m * n * k
     tops = ops / (ms_per_step * 1e-3) / 1e12
