@@ -1,25 +1,31 @@
 """Benchmark of the W4A8 hot path on one MI355X.
 
-Default workload (decode-shaped, HBM-bound): A bf16 [8, 4096] ~ N(0,1) with 0.1%
-outliers x20, W bf16 [4096, 4096] ~ N(0, 0.02^2) packed once to two-level int4
-(group 64).  One step = w4a8_gemm_bf16act: per-token int8 quantization of A plus
-the W4A8 GEMM with bf16 output (for m <= 16 one kernel does both).  Weight
-packing is offline (once per weight) and not part of a step.  The steps are
-captured into a HIP graph and the timed region replays it, so host-side launch
-cost does not stand in for device time.
+Default workload: the 70B-like FFN-down layer at M = 2048 (K = 28672,
+N = 8192), the largest configuration, MFMA-bound.  A bf16 [2048, 28672] unit
+Student t(3); W bf16 [8192, 28672] ~ N(0, 0.02^2) packed once to two-level
+int4 (group 64).  One step = w4a8_gemm_bf16act: per-token int8 quantization of
+A plus the W4A8 GEMM with bf16 output (for m <= 16 one kernel does both).
+Weight packing is offline (once per weight) and not part of a step.  The steps
+are captured into a HIP graph and the timed region replays it, so host-side
+launch cost does not stand in for device time.  Exactly --warmup untimed steps
+run first (one eager step loads the kernels, the rest replay graphs), then
+exactly --steps timed steps.
 
 Inputs are resident in HBM before timing.  To keep the 256 MB MALL and the L2s
 from serving the weights, each step uses the next of R distinct copies of the
 packed weights and activations (R copies total > 512 MB).
 
 Printed: one JSON line with the step throughput (TOPS = 2*M*N*K / step time),
-the dominant kernel's roofline (algorithmic bytes per launch / average launch
-time from HIP events on the launch stream), the standalone quantizer workload
-(64M bf16 elements, block 32 and 128: GB/s, dequantization round trip and its
-MSE), the extension paths (LQQ weights, W8A8 against W4A8 on a memory-bound and
-a compute-bound shape, per-block activation scales in the GEMM, the EQuARX
-dequantize-add-requantize step), and the CPU oracle timed on the host cores on
-a bounded sample (cpu_baseline).
+the dominant kernel's roofline (algorithmic ops or bytes per launch / average
+launch time from HIP events on the launch stream, against the vendor peak and
+against references measured in the same run: a device copy and an MFMA-only
+loop with its shader clock), the other workloads (decode, prefill, FFN-down
+M = 1 and 64) as sub-objects with their own rooflines, the standalone
+quantizer (64M bf16 elements, block 32 and 128: GB/s, dequantization round
+trip and its MSE), the extension paths (LQQ weights, W8A8 against W4A8 on
+memory-bound and compute-bound shapes, per-block activation scales in the
+GEMM, the EQuARX dequantize-add-requantize step), and the CPU oracle timed on
+the host cores on a bounded sample (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -44,11 +50,16 @@ METRIC = "W4A8 GEMM TOPS + quantizer GB/s; % of int8-MFMA / HBM roofline, 1 MI35
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=400)
-    p.add_argument("--workload", default="decode",
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="ffn_down_m2048",
                    choices=["decode", "prefill", "ffn_down_m1", "ffn_down_m64", "ffn_down_m2048",
                             "tiny"])
+    p.add_argument("--sub-steps", type=int, default=50,
+                   help="timed steps of each other workload (sub-objects of the line)")
+    p.add_argument("--sub-warmup", type=int, default=50)
+    p.add_argument("--no-subworkloads", action="store_true")
+    p.add_argument("--no-probes", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-quantizer", action="store_true")
     p.add_argument("--no-extensions", action="store_true")
@@ -195,6 +206,184 @@ def cpu_baseline(a_bits, w_bits, spec, seconds):
             }}
 
 
+def mfma_probe_leg(torch, w4a8, dev, stream, reps=10):
+    """The int8 matrix-core reference (MFMA-only loop built with the library): one
+    workgroup of 8 wavefronts per compute unit, timed with HIP events on the
+    launch stream; the shader clock is read inside the kernel."""
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 4096
+    for _ in range(3):
+        w4a8.probe_mfma_i8(ncu, iters, device=dev, stream=stream)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        ops, _, clocks = w4a8.probe_mfma_i8(ncu, iters, device=dev, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    ticks, rt = [int(v) for v in clocks.cpu().tolist()]
+    clock_ghz = ticks / rt * 0.1 if rt > 0 else None
+    tops = ops / (ms * 1e-3) / 1e12
+    res = {"kind": "int8 MFMA-only loop (w4a8_probe_mfma_i8), 8 wavefronts per CU",
+           "compute_units": ncu, "kernel_ms": ms, "achieved": tops, "unit": "TFLOP/s",
+           "frac_of_spec": tops / INT8_PEAK_TOPS, "clock_ghz": clock_ghz}
+    if clock_ghz:
+        res["peak_at_clock"] = ncu * 8192 * clock_ghz * 1e9 / 1e12
+    return res
+
+
+def measure_workload(torch, w4a8, dev, name, a_bits, w_bits, spec, steps, warmup,
+                     packed=None, probes=None):
+    """One workload: `warmup` untimed steps, then exactly `steps` timed steps, each
+    step = w4a8_gemm_bf16act (per-token quantization of A + the W4A8 GEMM) over
+    the next of R rotating weight/activation copies (> 512 MB in rotation).
+    Returns the step time, the step throughput and the dominant kernel's roofline."""
+    m, n, k = spec["m"], spec["n"], spec["k"]
+    out_dtype = torch.bfloat16 if spec["out"] == "bf16" else torch.float32
+    out_bytes = 2 if spec["out"] == "bf16" else 4
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    a0 = to_dev(a_bits)
+    wp0, gs0, cs0 = packed if packed is not None else w4a8.pack_w4_grouped(to_dev(w_bits))
+    per_copy = wp0.numel() + gs0.numel() + 4 * cs0.numel() + 2 * m * k
+    copies = n_copies(per_copy)
+    wps = [wp0] + [wp0.clone() for _ in range(copies - 1)]
+    gss = [gs0] + [gs0.clone() for _ in range(copies - 1)]
+    css = [cs0] + [cs0.clone() for _ in range(copies - 1)]
+    acts = [a0] + [a0.clone() for _ in range(copies - 1)]
+    # codes and scales of the quantized activations, then (16 < m <= 64, large K)
+    # the int32 partial sums of the split-K GEMM
+    ws_base = w4a8.workspace_bytes(m, k)
+    split = w4a8.gemm_workspace_bytes(m, n, k) > 0
+    wss = [torch.empty(w4a8.workspace_bytes(m, k, n), dtype=torch.uint8, device=dev)
+           for _ in range(copies)]
+    out = torch.empty((m, n), dtype=out_dtype, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(r, st):
+        # one pass of the path: per-token quantization of A + W4A8 GEMM
+        w4a8.w4a8_gemm_bf16act(acts[r], wps[r], gss[r], css[r], n, out=out, workspace=wss[r],
+                               stream=st)
+
+    def gemm_only(r, st):
+        a_q, a_s = w4a8.workspace_views(wss[r], m, k)
+        if split:
+            w4a8.w4a8_gemm_ws(a_q, a_s, wps[r], gss[r], css[r], n, out=out,
+                              workspace=wss[r][ws_base:], stream=st)
+        else:
+            w4a8.w4a8_gemm(a_q, a_s, wps[r], gss[r], css[r], n, out=out, stream=st)
+
+    def capture(fn, count=copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            s = torch.cuda.current_stream()
+            for r in range(count):
+                fn(r, s)
+        return g
+
+    # Warmup: exactly `warmup` untimed steps.  The first is an eager step on
+    # copy 0 (it loads the kernels before graph capture); the others replay
+    # graphs: whole graphs of `copies` steps, then a graph of the first
+    # (count mod copies) steps, captured beforehand.  The timed region replays
+    # exactly `steps` steps the same way.
+    eager = 1 if warmup >= 1 else 0
+    if eager:
+        step(0, stream)
+        torch.cuda.synchronize()
+    g_step = capture(step)
+    warm_graph = warmup - eager
+    partial = {r: capture(step, r) for r in {steps % copies, warm_graph % copies} if r}
+
+    def run_steps(count):
+        for _ in range(count // copies):
+            g_step.replay()
+        if count % copies:
+            partial[count % copies].replay()
+
+    run_steps(warm_graph)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    run_steps(steps)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / steps
+
+    # Dominant kernel: with m <= 16 the step is one fused kernel (quantization in
+    # the GEMM's prologue), so its average duration is the step time; otherwise
+    # the GEMM launches alone are replayed from their own graph (after one
+    # untimed replay) and timed with HIP events on the same stream (with split
+    # K: the K-sliced GEMM and the pass that sums its partials, together).
+    fused = m <= 16
+    if fused:
+        gemm_ms = ms_per_step
+        gemm_launches = steps
+    else:
+        g_gemm = capture(gemm_only)
+        g_gemm.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        reps = max(1, steps // copies)
+        e0.record(stream)
+        for _ in range(reps):
+            g_gemm.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gemm_ms = e0.elapsed_time(e1) / (reps * copies)
+        gemm_launches = reps * copies
+
+    ops = 2.0 * m * n * k
+    tops = ops / (ms_per_step * 1e-3) / 1e12
+    gemm_bytes = gemm_algorithmic_bytes(m, n, k, out_bytes, fused)
+    hbm_bound = m <= 64
+    if hbm_bound:
+        achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS}
+        if probes and probes.get("copy_gbps"):
+            roof["probe"] = {"kind": "256 MiB device copy, read + written",
+                             "achieved": probes["copy_gbps"], "unit": "GB/s",
+                             "frac_of_probe": achieved / probes["copy_gbps"]}
+    else:
+        achieved = ops / (gemm_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                "frac": achieved / INT8_PEAK_TOPS}
+        mp = (probes or {}).get("mfma")
+        if mp:
+            roof["probe"] = {"kind": mp["kind"], "achieved": mp["achieved"], "unit": "TFLOP/s",
+                             "frac_of_probe": achieved / mp["achieved"],
+                             "clock_ghz": mp["clock_ghz"]}
+    if split:
+        kernel_key = "gemm_splitk"
+    elif hbm_bound:
+        kernel_key = "gemm_skinny_fused" if fused else "gemm_skinny"
+    else:
+        kernel_key = "gemm_tiled"
+    roof["kernel"] = kernel_key
+    if split:
+        roof["kernel_launches"] = ["gemm_tiled_kernel over K slices", "splitk_finalize_kernel"]
+        roof["splitk_partial_bytes"] = w4a8.gemm_workspace_bytes(m, n, k)
+    roof["kernel_ms"] = gemm_ms
+    roof["kernel_launches_timed"] = gemm_launches
+    roof["algorithmic_bytes_per_launch"] = gemm_bytes
+    roof["algorithmic_ops_per_launch"] = ops
+    roof["traffic"] = profile_traffic(kernel_key, name)
+    res = {"workload": f"{name} W4A8 GEMM M={m} K={k} N={n}, per-token int8 activations "
+                       f"(quantized in the call), int4 weights group 64, {spec['out']} out",
+           "m": m, "n": n, "k": k, "steps": steps, "warmup": warmup, "ms_per_step": ms_per_step,
+           "value": tops, "unit": "TOPS", "weight_copies_rotated": copies, "roofline": roof}
+    del wps, gss, css, acts, wss, out, g_step, partial
+    return res
+
+
+SUB_WORKLOADS = ["ffn_down_m1", "ffn_down_m64", "decode", "prefill"]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -216,159 +405,78 @@ def main():
         print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": 4 * x.numel(),
                           "bytes_written_per_launch": 4 * x.numel(), "launches": 5}))
         return
-    a_bits, w_bits, spec = inputs.workload_inputs(args.workload, seed=0)
-    m, n, k = spec["m"], spec["n"], spec["k"]
-    out_dtype = torch.bfloat16 if spec["out"] == "bf16" else torch.float32
-    out_bytes = 2 if spec["out"] == "bf16" else 4
-
-    def to_dev(bits):
-        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
-
-    a0 = to_dev(a_bits)
-    wp0, gs0, cs0 = w4a8.pack_w4_grouped(to_dev(w_bits))
-    per_copy = wp0.numel() + gs0.numel() + 4 * cs0.numel() + 2 * m * k
-    copies = max(2, min(64, (512 << 20) // per_copy + 1))
-    wps = [wp0] + [wp0.clone() for _ in range(copies - 1)]
-    gss = [gs0] + [gs0.clone() for _ in range(copies - 1)]
-    css = [cs0] + [cs0.clone() for _ in range(copies - 1)]
-    acts = [a0] + [a0.clone() for _ in range(copies - 1)]
-    # codes and scales of the quantized activations, then (16 < m <= 64, large K)
-    # the int32 partial sums of the split-K GEMM
-    ws_base = w4a8.workspace_bytes(m, k)
-    split = w4a8.gemm_workspace_bytes(m, n, k) > 0
-    wss = [torch.empty(w4a8.workspace_bytes(m, k, n), dtype=torch.uint8, device=dev)
-           for _ in range(copies)]
-    out = torch.empty((m, n), dtype=out_dtype, device=dev)
-
-    def step(r, stream):
-        # one pass of the path: per-token quantization of A + W4A8 GEMM
-        w4a8.w4a8_gemm_bf16act(acts[r], wps[r], gss[r], css[r], n, out=out, workspace=wss[r],
-                               stream=stream)
-
-    def gemm_only(r, stream):
-        a_q, a_s = w4a8.workspace_views(wss[r], m, k)
-        if split:
-            w4a8.w4a8_gemm_ws(a_q, a_s, wps[r], gss[r], css[r], n, out=out,
-                              workspace=wss[r][ws_base:], stream=stream)
-        else:
-            w4a8.w4a8_gemm(a_q, a_s, wps[r], gss[r], css[r], n, out=out, stream=stream)
-
-    # One eager step per weight copy on a side stream, then capture `copies`
-    # steps (one per weight copy) into one HIP graph; the rest of the warmup
-    # and the timed region replay it, with a graph of the first K mod copies
-    # steps for a remainder, so exactly W steps run untimed (at least the
-    # `copies` eager ones) and exactly K are timed.  Under sustained load the
-    # first few hundred steps run slower (clocks settle), so the warmup is in
-    # steps of the graph itself.
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        for i in range(copies):
-            step(i, side)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-
-    def capture(fn, count=copies):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            s = torch.cuda.current_stream()
-            for r in range(count):
-                fn(r, s)
-        return g
-
-    def run_steps(count):
-        """Replay exactly `count` steps: whole graphs of `copies` steps, then a
-        graph of the first count % copies steps (captured beforehand)."""
-        for _ in range(count // copies):
-            g_step.replay()
-        if count % copies:
-            partial[count % copies].replay()
-
-    g_step = capture(step)
-    steps = max(1, args.steps)
-    warm_graph = max(0, args.warmup - copies)   # the eager priming ran `copies` steps
-    partial = {r: capture(step, r) for r in {steps % copies, warm_graph % copies} if r}
     stream = torch.cuda.current_stream()
-    run_steps(warm_graph)
-    torch.cuda.synchronize()
-    warmup_steps = max(args.warmup, copies)           # untimed steps actually run
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    run_steps(steps)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / steps
 
-    # Dominant kernel: with m <= 16 the step is one fused kernel (quantization in
-    # the GEMM's prologue), so its average duration is the step time; otherwise
-    # the GEMM launches alone are replayed from their own graph and timed (with
-    # split K: the K-sliced GEMM and the pass that sums its partials, together).
-    fused = m <= 16
-    if fused:
-        gemm_ms = ms_per_step
-    else:
-        g_gemm = capture(gemm_only)
-        g_gemm.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        reps = max(1, steps // copies)
-        e0.record(stream)
-        for _ in range(reps):
-            g_gemm.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        gemm_ms = e0.elapsed_time(e1) / (reps * copies)
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
-    ops = 2.0 * m * n * k
-    tops = ops / (ms_per_step * 1e-3) / 1e12
-    gemm_bytes = gemm_algorithmic_bytes(m, n, k, out_bytes, fused)
-    hbm_bound = m <= 64
-    if hbm_bound:
-        achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBPS}
-        # the same against a measured reference on this GPU
-        probe = copy_probe_gbps(torch, dev)
-        roof["probe"] = {"kind": "256 MiB device copy, read + written", "achieved": probe,
-                         "unit": "GB/s", "frac_of_probe": achieved / probe}
-    else:
-        achieved = ops / (gemm_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-                "frac": achieved / INT8_PEAK_TOPS}
-    if split:
-        kernel_key = "gemm_splitk"
-    elif hbm_bound:
-        kernel_key = "gemm_skinny_fused" if fused else "gemm_skinny"
-    else:
-        kernel_key = "gemm_tiled"
-    roof["kernel"] = kernel_key
-    if split:
-        roof["kernel_launches"] = ["gemm_tiled_kernel over K slices", "splitk_finalize_kernel"]
-        roof["splitk_partial_bytes"] = w4a8.gemm_workspace_bytes(m, n, k)
-    roof["kernel_ms"] = gemm_ms
-    roof["algorithmic_bytes_per_launch"] = gemm_bytes
-    roof["traffic"] = profile_traffic(kernel_key, args.workload)
+    # Measured references on this GPU: a device copy (HBM) and the MFMA-only loop.
+    probes = {}
+    if not args.no_probes:
+        probes["copy_gbps"] = copy_probe_gbps(torch, dev)
+        probes["mfma"] = mfma_probe_leg(torch, w4a8, dev, stream)
+        log("probes done")
 
+    a_bits, w_bits, spec = inputs.workload_inputs(args.workload, seed=0)
+    head = measure_workload(torch, w4a8, dev, args.workload, a_bits, w_bits, spec,
+                            max(1, args.steps), max(0, args.warmup), probes=probes)
+    log(f"{args.workload}: {head['ms_per_step'] * 1e3:.1f} us/step")
+    m, n, k = spec["m"], spec["n"], spec["k"]
     line = {
-        "metric": METRIC, "value": tops, "unit": "TOPS", "n_gpus": 1, "steps": steps,
-        "warmup": warmup_steps, "ms_per_step": ms_per_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
-        "config": {"workload": f"{args.workload} W4A8 GEMM M={m} K={k} N={n}, per-token int8 "
-                               f"activations, int4 weights group 64, {spec['out']} out",
-                   "m": m, "n": n, "k": k, "group": 64, "weight_copies_rotated": copies,
-                   "hip_graph_steps": copies, "parallelism": "single GPU"},
-        "roofline": roof,
+        "metric": METRIC, "value": head["value"], "unit": "TOPS", "n_gpus": 1,
+        "steps": head["steps"], "warmup": head["warmup"], "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": head["workload"], "m": m, "n": n, "k": k, "group": 64,
+                   "weight_copies_rotated": head["weight_copies_rotated"],
+                   "parallelism": "single GPU"},
+        "roofline": head["roofline"],
     }
+    if probes:
+        line["probes"] = {"hbm_copy_gbps": probes["copy_gbps"], "mfma": probes["mfma"]}
+
+    if not args.no_subworkloads:
+        # The other workloads of the path, each with its own roofline.  The FFN
+        # shapes share the head workload's weights when it is an FFN shape.
+        subs = {}
+        ffn_packed = None
+        head_ffn = args.workload.startswith("ffn_down")
+        for name in SUB_WORKLOADS:
+            if name == args.workload:
+                continue
+            packed = None
+            if name.startswith("ffn_down") and head_ffn:
+                # same weights (seed 0, 8192 x 28672): packed once, shared
+                sspec = inputs.WORKLOADS[name]
+                sa = inputs.activations(sspec["m"], sspec["k"], 0, sspec["dist"],
+                                        sspec["outlier_frac"])
+                sw = w_bits
+                if ffn_packed is None:
+                    wdev = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+                    ffn_packed = w4a8.pack_w4_grouped(wdev)
+                    del wdev
+                packed = ffn_packed
+            else:
+                sa, sw, sspec = inputs.workload_inputs(name, seed=0)
+            subs[name] = measure_workload(torch, w4a8, dev, name, sa, sw, sspec,
+                                          args.sub_steps, args.sub_warmup, packed=packed,
+                                          probes=probes)
+            log(f"{name}: {subs[name]['ms_per_step'] * 1e3:.2f} us/step")
+        del ffn_packed
+        torch.cuda.empty_cache()
+        line["workloads"] = subs
 
     if not args.no_quantizer:
         line["quantizer"] = quantizer_leg(torch, w4a8, inputs, dev, stream)
+        log("quantizer done")
     if not args.no_extensions:
-        line["extensions"] = extensions_leg(torch, w4a8, inputs, dev)
+        line["extensions"] = extensions_leg(
+            torch, w4a8, inputs, dev,
+            ffn_w_bits=w_bits if args.workload.startswith("ffn_down") else None)
+        log("extensions done")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(a_bits, w_bits, spec, args.cpu_seconds)
-        line["cpu_baseline"]["gpu_over_cpu"] = tops / line["cpu_baseline"]["value"]
+        line["cpu_baseline"]["gpu_over_cpu"] = head["value"] / line["cpu_baseline"]["value"]
     print(json.dumps(line), flush=True)
 
 
@@ -418,7 +526,7 @@ def quantizer_leg(torch, w4a8, inputs, dev, stream, reps=20):
     return res
 
 
-def extensions_leg(torch, w4a8, inputs, dev):
+def extensions_leg(torch, w4a8, inputs, dev, ffn_w_bits=None):
     """The extension paths, each timed from a HIP graph over rotating buffer sets:
     LQQ weights (decode shape, fused step), W8A8 against W4A8 (decode: memory-bound;
     prefill: compute-bound, int8 activations), the GEMM with per-block activation
@@ -506,6 +614,37 @@ def extensions_leg(torch, w4a8, inputs, dev):
                                   "frac": ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS,
                                   "per_token_ms": ms4}
     del sets4, a, w
+
+    # ---- the regime claim where the weights dominate: 70B FFN-down weights
+    # (8192 x 28672), fused per-token activations, M = 1 and M = 16
+    n, k = 8192, 28672
+    wf = ffn_w_bits if ffn_w_bits is not None else inputs.weights(n, k, 0)
+    w = bf16_dev(wf)
+    w4p, g4, c4 = w4a8.pack_w4_grouped(w)
+    c4n = n_copies(w4p.numel() + g4.numel())
+    sets4 = [(w4p, g4, c4)] + [(w4p.clone(), g4.clone(), c4.clone()) for _ in range(c4n - 1)]
+    w8p, c8 = w4a8.pack_w8_channel(w)
+    del w
+    c8n = n_copies(w8p.numel())
+    sets8 = [(w8p, c8)] + [(w8p.clone(), c8.clone()) for _ in range(c8n - 1)]
+    for m in (1, 16):
+        a = bf16_dev(inputs.activations(m, k, 0, "student_t"))
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(w4a8.workspace_bytes(m, k, n), dtype=torch.uint8, device=dev)
+        ms4 = time_graph(torch, lambda r, st: w4a8.w4a8_gemm_bf16act(
+            a, *sets4[r], n, out=out, workspace=ws, stream=st), c4n, 10)
+        ms8 = time_graph(torch, lambda r, st: w4a8.w8a8_gemm_bf16act(
+            a, *sets8[r], n, out=out, workspace=ws, stream=st), c8n, 10)
+        act_bytes = 2 * m * k + m * n * 2 + 4 * n
+        b4 = n * k // 2 + n * (k // 64) + act_bytes
+        b8 = n * k + act_bytes
+        res[f"w8a8_vs_w4a8_ffn_down_m{m}"] = {
+            "shape": [m, n, k], "w4a8_ms": ms4, "w8a8_ms": ms8, "w4a8_speedup": ms8 / ms4,
+            "w4a8_achieved": b4 / (ms4 * 1e-3) / 1e9, "w8a8_achieved": b8 / (ms8 * 1e-3) / 1e9,
+            "unit": "GB/s", "peak": HBM_PEAK_GBPS}
+        del a, out, ws
+    del sets4, sets8, w4p, g4, c4, w8p, c8
+    torch.cuda.empty_cache()
 
     # ---- EQuARX receive step on the quantizer's 64M elements
     qspec = inputs.QUANTIZER

@@ -34,11 +34,16 @@
  *   - Argument errors are detected before anything is launched; then nothing
  *     is written and a non-zero status is returned.  A failed launch returns
  *     W4A8_ERR_HIP.  Faults during execution surface at the caller's next
- *     synchronization.  With the environment variable W4A8_DEBUG=1 every
- *     call synchronizes its stream and reports execution errors as
- *     W4A8_ERR_HIP.
+ *     synchronization.
  *   - Empty inputs (rows == 0, m == 0, n == 0) are valid and do nothing.
  *   - NaN or infinite inputs are outside the contract (results unspecified).
+ *   - Debug mode (environment variable W4A8_DEBUG=1, read on every call):
+ *     before launching, a call synchronizes its stream, copies its floating
+ *     point inputs (bf16 activations or weights, binary32 scales or partial
+ *     sums) to host memory and returns W4A8_ERR_NONFINITE, writing nothing, if
+ *     any element is NaN or infinite; after launching it synchronizes again and
+ *     reports execution errors as W4A8_ERR_HIP.  Debug mode is slow (host
+ *     scans) and meant for development only.
  */
 #ifndef W4A8_H
 #define W4A8_H
@@ -70,7 +75,8 @@ typedef enum {
     W4A8_ERR_SHAPE = 2,       /* negative size or a divisibility rule is broken */
     W4A8_ERR_UNSUPPORTED = 3, /* valid request this build does not implement */
     W4A8_ERR_MISALIGNED = 4,  /* a pointer is not 16-byte aligned */
-    W4A8_ERR_HIP = 5          /* the HIP runtime reported an error */
+    W4A8_ERR_HIP = 5,         /* the HIP runtime reported an error */
+    W4A8_ERR_NONFINITE = 6    /* debug mode only: a floating point input holds NaN or Inf */
 } w4a8_status;
 
 typedef enum {
@@ -353,6 +359,26 @@ w4a8_status dequant_add_requant(const int8_t *q_in, const float *s_in, const voi
                                 w4a8_dtype x_dtype, int64_t rows, int64_t cols, int32_t block,
                                 float *sum_out, int8_t *q_out, float *s_out,
                                 hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Measurement aid (not part of the method): the int8 matrix-core reference
+ * that the GEMMs' utilisation is compared with, and the shader clock.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Runs `workgroups` workgroups of 8 wavefronts (two per SIMD with one per
+ * compute unit); each wavefront does `iters` rounds of 16 independent
+ * v_mfma_i32_16x16x64_i8 products, i.e. workgroups * iters * 4,194,304 int8
+ * operations (a multiply-add counts 2) and nothing else.
+ *   sink    int32 [workgroups * 512] (output; the accumulators' sums, so the
+ *           loop is not removed)
+ *   clocks  uint64 [2] (output): shader clock counter ticks (s_memtime) and
+ *           100 MHz real-time ticks (s_memrealtime) over one wavefront's loop;
+ *           clock (Hz) = clocks[0] / clocks[1] * 1e8.
+ * Requires workgroups in [1, 65535] and iters >= 1 (W4A8_ERR_SHAPE).
+ */
+w4a8_status w4a8_probe_mfma_i8(int64_t workgroups, int32_t iters, int32_t *sink,
+                               uint64_t *clocks, hipStream_t stream);
 
 #ifdef __cplusplus
 }

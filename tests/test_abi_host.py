@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "w4a8.h")
 LIB = os.path.join(ROOT, "w4a8_quantized_gemm_quantize_amd", "libw4a8.so")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP = range(6)
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP, ERR_NONFINITE = range(7)
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libw4a8.so not built")
 
@@ -77,7 +77,7 @@ def test_versions_and_status_strings(lib):
     assert lib.w4a8_abi_version() == 1
     assert lib.w4a8_pack_layout_version() == 1
     seen = set()
-    for s in range(6):
+    for s in range(7):
         txt = lib.w4a8_status_string(s).decode()
         assert txt and txt not in seen
         seen.add(txt)
@@ -270,3 +270,14 @@ def test_dequant_add_requant_validation(ext):
     assert f(A, B, C, 2, 4, 64, 32, D, E, A, NUL) == ERR_UNSUPPORTED  # int32 partial sums
     assert f(A, B, NUL, 0, 4, 64, 32, D, E, A, NUL) == ERR_NULL
     assert f(A, B, C, 1, 4, 64, 32, MIS, E, A, NUL) == ERR_MISALIGNED  # sum_out misaligned
+
+
+def test_mfma_probe_validation(lib):
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    f = lib.w4a8_probe_mfma_i8
+    f.argtypes = [I64, I32, P, P, P]
+    assert f(0, 10, A, B, NUL) == ERR_SHAPE
+    assert f(65536, 10, A, B, NUL) == ERR_SHAPE
+    assert f(256, 0, A, B, NUL) == ERR_SHAPE
+    assert f(256, 10, NUL, B, NUL) == ERR_NULL
+    assert f(256, 10, A, MIS, NUL) == ERR_MISALIGNED

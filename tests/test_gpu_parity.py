@@ -137,7 +137,7 @@ GEMM_SHAPES = [
     (64, 64, 448),
     (65, 48, 192),      # smallest tiled-path M, ragged N vs the workgroup tile
     (200, 272, 384),    # ragged M and N
-    (256, 512, 1024),
+    (256, 512, 1024),   # few tiles: the 128 x 256 launch only (no 256 x 256 tile)
     (129, 144, 4160),   # K = 32.5 chunks
     (37, 8192, 1088),   # skinny path with row splits (>= 512 tiles), ragged M, half chunk
     (64, 8208, 640),    # row splits, odd tile count (last workgroup half empty)
@@ -279,8 +279,8 @@ def test_gemm_extreme_codes_do_not_overflow(w4a8):
     (8, 4096, 4096),     # decode shape: quantization fused into the GEMM kernel
     (3, 64, 192),        # odd row count, trailing half chunk
     (13, 48, 1024),
-    (1, 32, 49088),      # largest one-row K kept in LDS
-    (2, 32, 24512),
+    (1, 32, 49088),      # 12 vectors per thread: beyond the fused form, quantize then GEMM
+    (2, 32, 24512),      # the same at two rows
     (16, 128, 4096),     # too large for the fused prologue: two kernels
     (100, 96, 512),      # tiled GEMM path
 ])

@@ -22,7 +22,7 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP = range(6)
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP, ERR_NONFINITE = range(7)
 F32, BF16, I32 = 0, 1, 2
 GROUP = 64
 N_TILE = 16
@@ -63,6 +63,7 @@ _SIGS = {
                             _P], ctypes.c_int),
     "dequant_add_requant": ([_P, _P, _P, ctypes.c_int, _I64, _I64, _I32, _P, _P, _P, _P],
                             ctypes.c_int),
+    "w4a8_probe_mfma_i8": ([_I64, _I32, _P, _P, _P], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -99,6 +100,17 @@ def _ptr(t):
 def _stream(stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _empty(stream, shape, dtype, device):
+    """A new tensor for a call enqueued on `stream`.  Allocated under that stream,
+    so torch's caching allocator does not hand the memory to work on another
+    stream while the call's kernels may still use it (a workspace the binding
+    creates is released when the call returns, before its kernels finish)."""
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
 
 
 def _check(fn, status):
@@ -164,9 +176,9 @@ def quantize_act_blockwise(x: torch.Tensor, block: int, q=None, scales=None, str
     _dev(x, torch.bfloat16, "x")
     rows, cols = x.shape
     if q is None:
-        q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+        q = _empty(stream, (rows, cols), dtype=torch.int8, device=x.device)
     if scales is None:
-        scales = torch.empty((rows, cols // block if block > 0 else 0), dtype=torch.float32,
+        scales = _empty(stream, (rows, cols // block if block > 0 else 0), dtype=torch.float32,
                              device=x.device)
     _sized("quantize_act_blockwise", q, (torch.int8,), rows * cols, "q")
     _sized("quantize_act_blockwise", scales, _F32, rows * _per(cols, block), "scales")
@@ -184,7 +196,7 @@ def dequantize_act_blockwise(q: torch.Tensor, scales: torch.Tensor, block: int,
     rows, cols = q.shape
     code = {torch.float32: F32, torch.bfloat16: BF16}[out_dtype]
     if out is None:
-        out = torch.empty((rows, cols), dtype=out_dtype, device=q.device)
+        out = _empty(stream, (rows, cols), dtype=out_dtype, device=q.device)
     _sized("dequantize_act_blockwise", scales, _F32, rows * _per(cols, block), "scales")
     _sized("dequantize_act_blockwise", out, (out_dtype,), rows * cols, "out")
     _check("dequantize_act_blockwise",
@@ -200,10 +212,10 @@ def pack_w4_grouped(w: torch.Tensor, group: int = GROUP, stream=None):
     _dev(w, torch.bfloat16, "w")
     n, k = w.shape
     dev = w.device
-    w_packed = torch.empty((n * k // 2,), dtype=torch.uint8, device=dev)
-    grp_scale = torch.empty((n * (k // group) if group > 0 else 0,), dtype=torch.uint8,
+    w_packed = _empty(stream, (n * k // 2,), dtype=torch.uint8, device=dev)
+    grp_scale = _empty(stream, (n * (k // group) if group > 0 else 0,), dtype=torch.uint8,
                             device=dev)
-    ch_scale = torch.empty((n,), dtype=torch.float32, device=dev)
+    ch_scale = _empty(stream, (n,), dtype=torch.float32, device=dev)
     _check("pack_w4_grouped",
            _lib.pack_w4_grouped(_ptr(w), n, k, group, _ptr(w_packed), _ptr(grp_scale),
                                 _ptr(ch_scale), _stream(stream)))
@@ -213,8 +225,8 @@ def pack_w4_grouped(w: torch.Tensor, group: int = GROUP, stream=None):
 def unpack_w4_grouped(w_packed, grp_scale, n: int, k: int, group: int = GROUP, stream=None):
     """Test hook: packed layout -> (q int8 [n, k], s_g uint8 [n, k/group]) canonical."""
     dev = w_packed.device
-    q = torch.empty((n, k), dtype=torch.int8, device=dev)
-    s_g = torch.empty((n, k // group), dtype=torch.uint8, device=dev)
+    q = _empty(stream, (n, k), dtype=torch.int8, device=dev)
+    s_g = _empty(stream, (n, k // group), dtype=torch.uint8, device=dev)
     _sized("unpack_w4_grouped", w_packed, _U8, n * k // 2, "w_packed")
     _sized("unpack_w4_grouped", grp_scale, _U8, n * _per(k, group), "grp_scale")
     _check("unpack_w4_grouped",
@@ -234,7 +246,7 @@ def w4a8_gemm(a_q, a_scale, w_packed, grp_scale, ch_scale, n: int, out_dtype=tor
     _dev(a_q, torch.int8, "a_q")
     m, k = a_q.shape
     if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=a_q.device)
+        out = _empty(stream, (m, n), dtype=out_dtype, device=a_q.device)
     _gemm_args("w4a8_gemm", m, n, k, a_scale, w_packed, 1, grp_scale, _U8, group, ch_scale, out)
     _check("w4a8_gemm",
            _lib.w4a8_gemm(_ptr(a_q), _ptr(a_scale), _ptr(w_packed), _ptr(grp_scale),
@@ -255,10 +267,10 @@ def w4a8_gemm_ws(a_q, a_scale, w_packed, grp_scale, ch_scale, n: int,
     _dev(a_q, torch.int8, "a_q")
     m, k = a_q.shape
     if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=a_q.device)
+        out = _empty(stream, (m, n), dtype=out_dtype, device=a_q.device)
     need = gemm_workspace_bytes(m, n, k)
     if workspace is None and need > 0:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=a_q.device)
+        workspace = _empty(stream, (need,), dtype=torch.uint8, device=a_q.device)
     _gemm_args("w4a8_gemm_ws", m, n, k, a_scale, w_packed, 1, grp_scale, _U8, group, ch_scale,
                out)
     _sized("w4a8_gemm_ws", workspace, _U8, 0, "workspace")
@@ -283,10 +295,10 @@ def w4a8_gemm_bf16act(a, w_packed, grp_scale, ch_scale, n: int, out_dtype=torch.
     _dev(a, torch.bfloat16, "a")
     m, k = a.shape
     if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+        out = _empty(stream, (m, n), dtype=out_dtype, device=a.device)
     need = workspace_bytes(m, k, n)
     if workspace is None:
-        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=a.device)
+        workspace = _empty(stream, (max(need, 16),), dtype=torch.uint8, device=a.device)
     _gemm_args("w4a8_gemm_bf16act", m, n, k, None, w_packed, 1, grp_scale, _U8, group, ch_scale,
                out)
     _sized("w4a8_gemm_bf16act", workspace, _U8, 0, "workspace")
@@ -313,10 +325,10 @@ def pack_w4_lqq(w: torch.Tensor, group: int = GROUP, stream=None):
     _dev(w, torch.bfloat16, "w")
     n, k = w.shape
     dev = w.device
-    w_packed = torch.empty((n * k // 2,), dtype=torch.uint8, device=dev)
-    grp_param = torch.empty((n * (k // group) if group > 0 else 0,), dtype=torch.int16,
+    w_packed = _empty(stream, (n * k // 2,), dtype=torch.uint8, device=dev)
+    grp_param = _empty(stream, (n * (k // group) if group > 0 else 0,), dtype=torch.int16,
                             device=dev)
-    ch_scale = torch.empty((n,), dtype=torch.float32, device=dev)
+    ch_scale = _empty(stream, (n,), dtype=torch.float32, device=dev)
     _check("pack_w4_lqq",
            _lib.pack_w4_lqq(_ptr(w), n, k, group, _ptr(w_packed), _ptr(grp_param),
                             _ptr(ch_scale), _stream(stream)))
@@ -326,9 +338,9 @@ def pack_w4_lqq(w: torch.Tensor, group: int = GROUP, stream=None):
 def unpack_w4_lqq(w_packed, grp_param, n: int, k: int, group: int = GROUP, stream=None):
     """Test hook -> (q_u4 uint8 [n, k], s_u8 uint8 [n, k/group], w_min int8 [n, k/group])."""
     dev = w_packed.device
-    q = torch.empty((n, k), dtype=torch.uint8, device=dev)
-    s_u8 = torch.empty((n, k // group), dtype=torch.uint8, device=dev)
-    w_min = torch.empty((n, k // group), dtype=torch.int8, device=dev)
+    q = _empty(stream, (n, k), dtype=torch.uint8, device=dev)
+    s_u8 = _empty(stream, (n, k // group), dtype=torch.uint8, device=dev)
+    w_min = _empty(stream, (n, k // group), dtype=torch.int8, device=dev)
     _sized("unpack_w4_lqq", w_packed, _U8, n * k // 2, "w_packed")
     _sized("unpack_w4_lqq", grp_param, _I16, n * _per(k, group), "grp_param")
     _check("unpack_w4_lqq",
@@ -342,7 +354,7 @@ def w4a8_gemm_lqq(a_q, a_scale, w_packed, grp_param, ch_scale, n: int,
     _dev(a_q, torch.int8, "a_q")
     m, k = a_q.shape
     if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=a_q.device)
+        out = _empty(stream, (m, n), dtype=out_dtype, device=a_q.device)
     _gemm_args("w4a8_gemm_lqq", m, n, k, a_scale, w_packed, 1, grp_param, _I16, group,
                ch_scale, out)
     _check("w4a8_gemm_lqq",
@@ -357,9 +369,9 @@ def w4a8_gemm_lqq_bf16act(a, w_packed, grp_param, ch_scale, n: int, out_dtype=to
     _dev(a, torch.bfloat16, "a")
     m, k = a.shape
     if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+        out = _empty(stream, (m, n), dtype=out_dtype, device=a.device)
     if workspace is None:
-        workspace = torch.empty((max(workspace_bytes(m, k, n), 16),), dtype=torch.uint8,
+        workspace = _empty(stream, (max(workspace_bytes(m, k, n), 16),), dtype=torch.uint8,
                                 device=a.device)
     _gemm_args("w4a8_gemm_lqq_bf16act", m, n, k, None, w_packed, 1, grp_param, _I16, group,
                ch_scale, out)
@@ -377,15 +389,15 @@ def pack_w8_channel(w: torch.Tensor, stream=None):
     """w bf16 [n, k] -> (w_packed int8 [n*k] tiled layout, ch_scale f32 [n])."""
     _dev(w, torch.bfloat16, "w")
     n, k = w.shape
-    w_packed = torch.empty((n * k,), dtype=torch.int8, device=w.device)
-    ch_scale = torch.empty((n,), dtype=torch.float32, device=w.device)
+    w_packed = _empty(stream, (n * k,), dtype=torch.int8, device=w.device)
+    ch_scale = _empty(stream, (n,), dtype=torch.float32, device=w.device)
     _check("pack_w8_channel",
            _lib.pack_w8_channel(_ptr(w), n, k, _ptr(w_packed), _ptr(ch_scale), _stream(stream)))
     return w_packed, ch_scale
 
 
 def unpack_w8_channel(w_packed, n: int, k: int, stream=None):
-    q8 = torch.empty((n, k), dtype=torch.int8, device=w_packed.device)
+    q8 = _empty(stream, (n, k), dtype=torch.int8, device=w_packed.device)
     _sized("unpack_w8_channel", w_packed, _U8, n * k, "w_packed")
     _check("unpack_w8_channel",
            _lib.unpack_w8_channel(_ptr(w_packed), n, k, _ptr(q8), _stream(stream)))
@@ -397,7 +409,7 @@ def w8a8_gemm(a_q, a_scale, w_packed, ch_scale, n: int, out_dtype=torch.bfloat16
     _dev(a_q, torch.int8, "a_q")
     m, k = a_q.shape
     if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=a_q.device)
+        out = _empty(stream, (m, n), dtype=out_dtype, device=a_q.device)
     _gemm_args("w8a8_gemm", m, n, k, a_scale, w_packed, 2, None, None, GROUP, ch_scale, out)
     _check("w8a8_gemm",
            _lib.w8a8_gemm(_ptr(a_q), _ptr(a_scale), _ptr(w_packed), _ptr(ch_scale), m, n, k,
@@ -410,9 +422,9 @@ def w8a8_gemm_bf16act(a, w_packed, ch_scale, n: int, out_dtype=torch.bfloat16, o
     _dev(a, torch.bfloat16, "a")
     m, k = a.shape
     if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+        out = _empty(stream, (m, n), dtype=out_dtype, device=a.device)
     if workspace is None:
-        workspace = torch.empty((max(workspace_bytes(m, k, n), 16),), dtype=torch.uint8,
+        workspace = _empty(stream, (max(workspace_bytes(m, k, n), 16),), dtype=torch.uint8,
                                 device=a.device)
     _gemm_args("w8a8_gemm_bf16act", m, n, k, None, w_packed, 2, None, None, GROUP, ch_scale, out)
     _sized("w8a8_gemm_bf16act", workspace, _U8, 0, "workspace")
@@ -432,7 +444,7 @@ def w4a8_gemm_blockact(a_q, a_scale, w_packed, grp_scale, ch_scale, n: int, bloc
     _dev(a_scale, torch.float32, "a_scale")
     m, k = a_q.shape
     if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=a_q.device)
+        out = _empty(stream, (m, n), dtype=out_dtype, device=a_q.device)
     _gemm_args("w4a8_gemm_blockact", 0, n, k, None, w_packed, 1, grp_scale, _U8, group,
                ch_scale, out)
     _sized("w4a8_gemm_blockact", a_scale, _F32, m * _per(k, block), "a_scale")
@@ -458,12 +470,12 @@ def dequant_add_requant(q_in, s_in, x, block: int, want_sum: bool = False, q_out
     rows, cols = q_in.shape
     dev = q_in.device
     if q_out is None:
-        q_out = torch.empty((rows, cols), dtype=torch.int8, device=dev)
+        q_out = _empty(stream, (rows, cols), dtype=torch.int8, device=dev)
     if s_out is None:
-        s_out = torch.empty((rows, cols // block if block > 0 else 0), dtype=torch.float32,
+        s_out = _empty(stream, (rows, cols // block if block > 0 else 0), dtype=torch.float32,
                             device=dev)
     if want_sum and sum_out is None:
-        sum_out = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+        sum_out = _empty(stream, (rows, cols), dtype=torch.float32, device=dev)
     fn = "dequant_add_requant"
     _sized(fn, s_in, _F32, rows * _per(cols, block), "s_in")
     _sized(fn, x, (x.dtype,), rows * cols, "x")
@@ -476,3 +488,17 @@ def dequant_add_requant(q_in, s_in, x, block: int, want_sum: bool = False, q_out
                                     block, _ptr(sum_out), _ptr(q_out), _ptr(s_out),
                                     _stream(stream)))
     return q_out, s_out, sum_out
+
+
+# -------------------------------------------------------- measurement aid --
+
+def probe_mfma_i8(workgroups: int, iters: int, device=None, stream=None):
+    """Int8 matrix-core reference loop: returns (ops, sink, clocks) where ops is
+    the int8 operation count of the launch and clocks (after the stream is
+    synchronized) holds [shader clock ticks, 100 MHz real-time ticks]."""
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    sink = _empty(stream, (workgroups * 512,), dtype=torch.int32, device=dev)
+    clocks = _empty(stream, (2,), dtype=torch.int64, device=dev)
+    _check("w4a8_probe_mfma_i8",
+           _lib.w4a8_probe_mfma_i8(workgroups, iters, _ptr(sink), _ptr(clocks), _stream(stream)))
+    return workgroups * iters * 4194304, sink, clocks

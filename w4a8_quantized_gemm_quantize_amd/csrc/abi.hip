@@ -1,11 +1,38 @@
 // abi.hip -- the extern "C" entry points of libw4a8.so (declared in w4a8.h):
 // argument validation, variant choice and launch on the caller's stream.
-// Nothing here allocates device memory or keeps state between calls.
+// Nothing here allocates device memory.  The only state kept between calls is
+// a per-device cache of the compute-unit count.
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <initializer_list>
+#include <vector>
+
 #include "w4a8.h"
 #include "launch.hpp"
+
+namespace w4a8 {
+
+int device_cu_count() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = -1;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int ncu = 0;
+    if (dev < 0 ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        ncu <= 0)
+        return 256;
+    if (dev < kMaxDevices) cache[dev].store(ncu, std::memory_order_relaxed);
+    return ncu;
+}
+
+}  // namespace w4a8
 
 namespace {
 
@@ -14,6 +41,43 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool debug_sync_enabled() {
     const char *v = getenv("W4A8_DEBUG");
     return v && v[0] == '1';
+}
+
+// A floating point input of a call: device pointer, element count, bf16 or binary32.
+struct FpInput {
+    const void *p;
+    size_t count;
+    bool bf16;
+};
+
+// Debug mode only: wait for the stream (the inputs may still be being
+// written), copy each floating point input to host memory in slices and look
+// for NaN or Inf (all exponent bits set).  W4A8_OK outside debug mode.
+w4a8_status debug_check_inputs(hipStream_t stream, std::initializer_list<FpInput> inputs) {
+    if (!debug_sync_enabled()) return W4A8_OK;
+    if (hipStreamSynchronize(stream) != hipSuccess) return W4A8_ERR_HIP;
+    constexpr size_t kSlice = size_t(1) << 22;   // elements per host copy
+    std::vector<uint32_t> host;
+    for (const FpInput &in : inputs) {
+        if (!in.p || in.count == 0) continue;
+        const size_t esize = in.bf16 ? 2 : 4;
+        for (size_t off = 0; off < in.count; off += kSlice) {
+            const size_t cnt = in.count - off < kSlice ? in.count - off : kSlice;
+            host.resize((cnt * esize + 3) / 4);
+            if (hipMemcpy(host.data(), (const uint8_t *)in.p + off * esize, cnt * esize,
+                          hipMemcpyDeviceToHost) != hipSuccess)
+                return W4A8_ERR_HIP;
+            if (in.bf16) {
+                const uint16_t *h = (const uint16_t *)host.data();
+                for (size_t i = 0; i < cnt; ++i)
+                    if ((h[i] & 0x7f80u) == 0x7f80u) return W4A8_ERR_NONFINITE;
+            } else {
+                for (size_t i = 0; i < cnt; ++i)
+                    if ((host[i] & 0x7f800000u) == 0x7f800000u) return W4A8_ERR_NONFINITE;
+            }
+        }
+    }
+    return W4A8_OK;
 }
 
 // Map a launch result to a status; with W4A8_DEBUG=1 also wait for the stream.
@@ -101,6 +165,7 @@ const char *w4a8_status_string(w4a8_status status) {
         case W4A8_ERR_UNSUPPORTED: return "unsupported argument";
         case W4A8_ERR_MISALIGNED: return "pointer not 16-byte aligned";
         case W4A8_ERR_HIP: return "HIP runtime error";
+        case W4A8_ERR_NONFINITE: return "non-finite input (debug check)";
     }
     return "unknown status";
 }
@@ -112,6 +177,8 @@ w4a8_status quantize_act_blockwise(const uint16_t *x, int64_t rows, int64_t cols
     if (rows == 0 || cols == 0) return W4A8_OK;
     if (!x || !q || !scales) return W4A8_ERR_NULL;
     if (!aligned16(x) || !aligned16(q) || !aligned16(scales)) return W4A8_ERR_MISALIGNED;
+    st = debug_check_inputs(stream, {{x, (size_t)(rows * cols), true}});
+    if (st != W4A8_OK) return st;
     return finish(w4a8::launch_quantize_act(x, rows, cols, block, q, scales, stream), stream);
 }
 
@@ -124,6 +191,8 @@ w4a8_status dequantize_act_blockwise(const int8_t *q, const float *scales, int64
     if (rows == 0 || cols == 0) return W4A8_OK;
     if (!q || !scales || !out) return W4A8_ERR_NULL;
     if (!aligned16(q) || !aligned16(scales) || !aligned16(out)) return W4A8_ERR_MISALIGNED;
+    st = debug_check_inputs(stream, {{scales, (size_t)(rows * (cols / block)), false}});
+    if (st != W4A8_OK) return st;
     return finish(w4a8::launch_dequantize_act(q, scales, rows, cols, block, out,
                                               out_dtype == W4A8_BF16, stream),
                   stream);
@@ -139,6 +208,8 @@ w4a8_status pack_w4_grouped(const uint16_t *w, int64_t n, int64_t k, int32_t gro
     if (!aligned16(ch_scale) ||
         (k > 0 && (!aligned16(w) || !aligned16(w_packed) || !aligned16(grp_scale))))
         return W4A8_ERR_MISALIGNED;
+    st = debug_check_inputs(stream, {{w, (size_t)(n * k), true}});
+    if (st != W4A8_OK) return st;
     return finish(w4a8::launch_pack_w4(w, n, k, w_packed, grp_scale, ch_scale, stream), stream);
 }
 
@@ -162,6 +233,8 @@ w4a8_status w4a8_gemm(const int8_t *a_q, const float *a_scale, const uint8_t *w_
                                      k, group, out, out_dtype);
     if (st != W4A8_OK) return st;
     if (m == 0 || n == 0) return W4A8_OK;
+    st = debug_check_inputs(stream, {{a_scale, (size_t)m, false}, {ch_scale, (size_t)n, false}});
+    if (st != W4A8_OK) return st;
     return finish(w4a8::launch_w4a8_gemm(a_q, a_scale, w_packed, grp_scale, ch_scale, m, n, k,
                                          out, (int)out_dtype, stream),
                   stream);
@@ -180,6 +253,8 @@ w4a8_status w4a8_gemm_ws(const int8_t *a_q, const float *a_scale, const uint8_t 
                                      k, group, out, out_dtype);
     if (st != W4A8_OK) return st;
     if (m == 0 || n == 0) return W4A8_OK;
+    st = debug_check_inputs(stream, {{a_scale, (size_t)m, false}, {ch_scale, (size_t)n, false}});
+    if (st != W4A8_OK) return st;
     const size_t need = w4a8_gemm_workspace_bytes(m, n, k);
     int32_t *partials = nullptr;
     if (need > 0) {
@@ -208,6 +283,8 @@ w4a8_status w4a8_gemm_bf16act(const uint16_t *a, const uint8_t *w_packed,
                                      k, group, out, out_dtype);
     if (st != W4A8_OK) return st;
     if (m == 0 || n == 0) return W4A8_OK;
+    st = debug_check_inputs(stream, {{a, (size_t)(m * k), true}, {ch_scale, (size_t)n, false}});
+    if (st != W4A8_OK) return st;
     int8_t *a_q;
     float *a_s;
     int32_t *partials;
@@ -230,6 +307,8 @@ w4a8_status pack_w4_lqq(const uint16_t *w, int64_t n, int64_t k, int32_t group,
     if (!aligned16(ch_scale) ||
         (k > 0 && (!aligned16(w) || !aligned16(w_packed) || !aligned16(grp_param))))
         return W4A8_ERR_MISALIGNED;
+    st = debug_check_inputs(stream, {{w, (size_t)(n * k), true}});
+    if (st != W4A8_OK) return st;
     return finish(w4a8::launch_pack_w4_lqq(w, n, k, w_packed, grp_param, ch_scale, stream),
                   stream);
 }
@@ -257,6 +336,8 @@ w4a8_status w4a8_gemm_lqq(const int8_t *a_q, const float *a_scale, const uint8_t
                                      k, group, out, out_dtype, W4A8_LQQ_K_MAX);
     if (st != W4A8_OK) return st;
     if (m == 0 || n == 0) return W4A8_OK;
+    st = debug_check_inputs(stream, {{a_scale, (size_t)m, false}, {ch_scale, (size_t)n, false}});
+    if (st != W4A8_OK) return st;
     return finish(w4a8::launch_w4a8_gemm_lqq(a_q, a_scale, w_packed, grp_param, ch_scale, m, n,
                                              k, out, (int)out_dtype, stream),
                   stream);
@@ -272,6 +353,8 @@ w4a8_status w4a8_gemm_lqq_bf16act(const uint16_t *a, const uint8_t *w_packed,
                                      group, out, out_dtype, W4A8_LQQ_K_MAX);
     if (st != W4A8_OK) return st;
     if (m == 0 || n == 0) return W4A8_OK;
+    st = debug_check_inputs(stream, {{a, (size_t)(m * k), true}, {ch_scale, (size_t)n, false}});
+    if (st != W4A8_OK) return st;
     int8_t *a_q;
     float *a_s;
     int32_t *partials;
@@ -292,6 +375,8 @@ w4a8_status pack_w8_channel(const uint16_t *w, int64_t n, int64_t k, int8_t *w_p
     if (!ch_scale || (k > 0 && (!w || !w_packed))) return W4A8_ERR_NULL;
     if (!aligned16(ch_scale) || (k > 0 && (!aligned16(w) || !aligned16(w_packed))))
         return W4A8_ERR_MISALIGNED;
+    st = debug_check_inputs(stream, {{w, (size_t)(n * k), true}});
+    if (st != W4A8_OK) return st;
     return finish(w4a8::launch_pack_w8(w, n, k, w_packed, ch_scale, stream), stream);
 }
 
@@ -312,6 +397,8 @@ w4a8_status w8a8_gemm(const int8_t *a_q, const float *a_scale, const int8_t *w_p
                                      W4A8_GROUP, out, out_dtype, W4A8_LQQ_K_MAX, false);
     if (st != W4A8_OK) return st;
     if (m == 0 || n == 0) return W4A8_OK;
+    st = debug_check_inputs(stream, {{a_scale, (size_t)m, false}, {ch_scale, (size_t)n, false}});
+    if (st != W4A8_OK) return st;
     return finish(w4a8::launch_w8a8_gemm(a_q, a_scale, w_packed, ch_scale, m, n, k, out,
                                          (int)out_dtype, stream),
                   stream);
@@ -325,6 +412,8 @@ w4a8_status w8a8_gemm_bf16act(const uint16_t *a, const int8_t *w_packed, const f
                                      W4A8_GROUP, out, out_dtype, W4A8_LQQ_K_MAX, false);
     if (st != W4A8_OK) return st;
     if (m == 0 || n == 0) return W4A8_OK;
+    st = debug_check_inputs(stream, {{a, (size_t)(m * k), true}, {ch_scale, (size_t)n, false}});
+    if (st != W4A8_OK) return st;
     int8_t *a_q;
     float *a_s;
     int32_t *partials;
@@ -348,6 +437,9 @@ w4a8_status w4a8_gemm_blockact(const int8_t *a_q, const float *a_scale, const ui
     if (st != W4A8_OK) return st;
     if ((k % block) != 0) return W4A8_ERR_SHAPE;
     if (m == 0 || n == 0) return W4A8_OK;
+    st = debug_check_inputs(stream,
+                            {{a_scale, (size_t)(m * (k / block)), false}, {ch_scale, (size_t)n, false}});
+    if (st != W4A8_OK) return st;
     return finish(w4a8::launch_w4a8_gemm_blockact(a_q, a_scale, w_packed, grp_scale, ch_scale, m,
                                                   n, k, block, out, (int)out_dtype, stream),
                   stream);
@@ -367,9 +459,22 @@ w4a8_status dequant_add_requant(const int8_t *q_in, const float *s_in, const voi
     if (!aligned16(q_in) || !aligned16(s_in) || !aligned16(x) || !aligned16(q_out) ||
         !aligned16(s_out) || (sum_out && !aligned16(sum_out)))
         return W4A8_ERR_MISALIGNED;
+    st = debug_check_inputs(stream, {{s_in, (size_t)(rows * (cols / block)), false},
+                                     {x, (size_t)(rows * cols), x_dtype == W4A8_BF16}});
+    if (st != W4A8_OK) return st;
     return finish(w4a8::launch_dequant_add_requant(q_in, s_in, x, x_dtype == W4A8_BF16, rows,
                                                    cols, block, sum_out, q_out, s_out, stream),
                   stream);
+}
+
+/* ------------------------------------------------------ measurement aid */
+
+w4a8_status w4a8_probe_mfma_i8(int64_t workgroups, int32_t iters, int32_t *sink,
+                               uint64_t *clocks, hipStream_t stream) {
+    if (workgroups < 1 || workgroups > 65535 || iters < 1) return W4A8_ERR_SHAPE;
+    if (!sink || !clocks) return W4A8_ERR_NULL;
+    if (!aligned16(sink) || !aligned16(clocks)) return W4A8_ERR_MISALIGNED;
+    return finish(w4a8::launch_mfma_probe(workgroups, iters, sink, clocks, stream), stream);
 }
 
 }  // extern "C"

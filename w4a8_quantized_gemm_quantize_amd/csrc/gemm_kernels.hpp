@@ -1276,11 +1276,7 @@ template <int WF>
 void launch_tiled_large(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
                         const uint8_t *grp_scale, const float *ch_scale, int64_t m, int64_t n,
                         int64_t k, void *out, int out_dtype, hipStream_t stream) {
-    int dev = 0, ncu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        ncu <= 0)
-        ncu = 256;
+    const int ncu = device_cu_count();
     const int64_t mt = (m + 255) / 256, ntb = (n + 255) / 256;
     auto rounds = [&](int64_t tiles) { return (tiles + ncu - 1) / ncu; };
     // cost in units of one round of large tiles; large-tile columns first
@@ -1370,10 +1366,7 @@ hipError_t launch_gemm_bf16act_fmt(const uint16_t *a, const uint8_t *w_packed,
     if (av > 0) {
         const size_t lds_bytes = (size_t)(m * (k + 16));
         const bool w16 = fused_waves(k) == 16;
-        int dev = 0, ncu = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            ncu = 0;
+        const int ncu = device_cu_count();
         // one workgroup per 16-channel tile: at most one per CU -> keep the floats
         const bool one_per_cu = n / kNTile <= (int64_t)ncu;
         if (av == 4 && w16 && one_per_cu)

@@ -6,6 +6,10 @@
 
 namespace w4a8 {
 
+// Compute units of the current device, queried once per device and cached
+// (the launchers size grids by it on every call).
+int device_cu_count();
+
 hipError_t launch_quantize_act(const uint16_t *x, int64_t rows, int64_t cols, int32_t block,
                                int8_t *q, float *scales, hipStream_t stream);
 hipError_t launch_dequantize_act(const int8_t *q, const float *scales, int64_t rows,
@@ -75,5 +79,9 @@ hipError_t launch_dequant_add_requant(const int8_t *q_in, const float *s_in, con
                                       bool x_bf16, int64_t rows, int64_t cols, int32_t block,
                                       float *sum_out, int8_t *q_out, float *s_out,
                                       hipStream_t stream);
+
+// int8 matrix-core reference loop (measurement aid).
+hipError_t launch_mfma_probe(int64_t workgroups, int32_t iters, int32_t *sink, uint64_t *clocks,
+                             hipStream_t stream);
 
 }  // namespace w4a8
