@@ -219,6 +219,32 @@ w4a8_status w4a8_gemm_bf16act(const uint16_t *a, const uint8_t *w_packed,
                               w4a8_dtype out_dtype, void *workspace, size_t ws_bytes,
                               hipStream_t stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as w4a8_gemm_bf16act, same arguments, rules and result bit for bit,
+ * with its workspace (activation codes and scales, and the split-K partials
+ * when the shape splits) in a static device array of the library instead of
+ * caller memory.  Nothing is allocated or freed by the call; the caller passes
+ * the inputs and `out` as usual.
+ *   - The array holds W4A8_NOALLOC_SCRATCH_BYTES (64 MiB) per device, placed
+ *     when the library's code is loaded on that device and kept until the
+ *     process ends.  A call whose workspace would exceed it,
+ *     w4a8_gemm_bf16act_workspace_bytes(m, k) + w4a8_gemm_workspace_bytes(m,
+ *     n, k) > W4A8_NOALLOC_SCRATCH_BYTES, returns W4A8_ERR_UNSUPPORTED before
+ *     touching the device (the 70B FFN-down shapes up to m = 2048 fit).
+ *   - Every call on a device shares that device's array and leaves its
+ *     contents behind: calls that overlap on one device (two streams, two
+ *     host threads) race and must be ordered by the caller.
+ *   - The array's address is looked up once per device, on the first call
+ *     with that device current (W4A8_ERR_HIP if that fails).
+ */
+#define W4A8_NOALLOC_SCRATCH_BYTES (64ll << 20)
+w4a8_status w4a8_gemm_bf16act_noalloc(const uint16_t *a, const uint8_t *w_packed,
+                                      const uint8_t *grp_scale, const float *ch_scale,
+                                      int64_t m, int64_t n, int64_t k, int32_t group, void *out,
+                                      w4a8_dtype out_dtype, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * LQQ weights: LiquidGEMM's own asymmetric 4-bit format ("LiquidGEMM" verdict
  * page, pith_extraction.key_machinery: INT8 weights shifted by the group

@@ -281,3 +281,16 @@ def test_mfma_probe_validation(lib):
     assert f(256, 0, A, B, NUL) == ERR_SHAPE
     assert f(256, 10, NUL, B, NUL) == ERR_NULL
     assert f(256, 10, A, MIS, NUL) == ERR_MISALIGNED
+
+
+def test_noalloc_validation(lib):
+    # shape and size errors are returned before the device is touched
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    f = lib.w4a8_gemm_bf16act_noalloc
+    f.argtypes = [P, P, P, P, I64, I64, I64, I32, P, ctypes.c_int, P]
+    assert f(A, B, C, D, 8, 64, 0, 64, E, 1, NUL) == ERR_SHAPE
+    assert f(A, B, C, D, -1, 64, 256, 64, E, 1, NUL) == ERR_SHAPE
+    assert f(A, B, C, D, 0, 64, 256, 64, E, 1, NUL) == OK
+    assert f(A, B, C, D, 4096, 64, 32768, 64, E, 1, NUL) == ERR_UNSUPPORTED  # 128 MiB of codes
+    assert f(A, NUL, C, D, 8, 64, 256, 64, E, 1, NUL) == ERR_NULL
+    assert f(A, B, C, D, 8, 64, 256, 64, MIS, 1, NUL) == ERR_MISALIGNED

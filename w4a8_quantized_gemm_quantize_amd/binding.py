@@ -64,6 +64,8 @@ _SIGS = {
     "dequant_add_requant": ([_P, _P, _P, ctypes.c_int, _I64, _I64, _I32, _P, _P, _P, _P],
                             ctypes.c_int),
     "w4a8_probe_mfma_i8": ([_I64, _I32, _P, _P, _P], ctypes.c_int),
+    "w4a8_gemm_bf16act_noalloc": ([_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, ctypes.c_int, _P],
+                                  ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -306,6 +308,25 @@ def w4a8_gemm_bf16act(a, w_packed, grp_scale, ch_scale, n: int, out_dtype=torch.
            _lib.w4a8_gemm_bf16act(_ptr(a), _ptr(w_packed), _ptr(grp_scale), _ptr(ch_scale), m,
                                   n, k, group, _ptr(out), _OUT[out.dtype], _ptr(workspace),
                                   workspace.numel(), _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def w4a8_gemm_bf16act_noalloc(a, w_packed, grp_scale, ch_scale, n: int, out,
+                              group: int = GROUP, stream=None):
+    """w4a8_gemm_bf16act with the library's static device workspace: the caller
+    passes `out` ([m, n] float32, bfloat16 or int32) and nothing is allocated.
+    Calls that overlap on one GPU share that workspace and race."""
+    _dev(a, torch.bfloat16, "a")
+    m, k = a.shape
+    _gemm_args("w4a8_gemm_bf16act_noalloc", m, n, k, None, w_packed, 1, grp_scale, _U8, group,
+               ch_scale, out)
+    _check("w4a8_gemm_bf16act_noalloc",
+           _lib.w4a8_gemm_bf16act_noalloc(_ptr(a), _ptr(w_packed), _ptr(grp_scale),
+                                          _ptr(ch_scale), m, n, k, group, _ptr(out),
+                                          _OUT[out.dtype], _stream(stream)))
     return out
 
 
