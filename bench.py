@@ -493,20 +493,11 @@ def quantizer_leg(torch, w4a8, inputs, dev, stream, reps=20):
         qs = [torch.empty((rows, cols), dtype=torch.int8, device=dev) for _ in range(2)]
         ss = [torch.empty((rows, cols // block), dtype=torch.float32, device=dev)
               for _ in range(2)]
-        for i in range(4):
-            w4a8.quantize_act_blockwise(xs[i % 2], block, q=qs[i % 2], scales=ss[i % 2],
-                                        stream=stream)
-        times = []
-        for i in range(reps):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            w4a8.quantize_act_blockwise(xs[i % 2], block, q=qs[i % 2], scales=ss[i % 2],
-                                        stream=stream)
-            e1.record(stream)
-            times.append((e0, e1))
-        torch.cuda.synchronize()
-        ms = float(np.mean([a.elapsed_time(b) for a, b in times]))
+        def quant(r, st, block=block, qs=qs, ss=ss):
+            w4a8.quantize_act_blockwise(xs[r], block, q=qs[r], scales=ss[r], stream=st)
+        # graph replays of the two input/output sets in turn, as for the GEMMs
+        # (per-call events would add the launch gaps to a 35-40 us kernel)
+        ms = time_graph(torch, quant, 2, reps)
         gbps = quantizer_algorithmic_bytes(rows * cols, block) / (ms * 1e-3) / 1e9
         entry = {"kernel_ms": ms, "achieved": gbps, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS}
         # dequantization round trip: q, scales -> fp32 and bf16; MSE against x

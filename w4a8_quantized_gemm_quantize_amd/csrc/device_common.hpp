@@ -135,6 +135,25 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// Maximum of a non-negative 32-bit value over aligned groups of LPB adjacent
+// lanes (LPB a power of two up to 64), returned to every lane of the group:
+// DPP quad swaps and half-row / row mirrors inside a row of 16 lanes (VALU
+// operations, no LDS traffic), then lane swaps across rows.
+template <int LPB>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+    if constexpr (LPB >= 2)
+        v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));
+    if constexpr (LPB >= 4)
+        v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));
+    if constexpr (LPB >= 8)
+        v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));
+    if constexpr (LPB >= 16)
+        v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));
+    if constexpr (LPB >= 32) v = max(v, (uint32_t)__shfl_xor((int)v, 16));
+    if constexpr (LPB >= 64) v = max(v, (uint32_t)__shfl_xor((int)v, 32));
+    return v;
+}
+
 // Rebuild 4 int8 weights q*s from a word of 4 nibbles (one per byte, low bits).
 // mul = s | s << 16, add = (128 - 8 s) * 0x01010101.
 __device__ __forceinline__ int dequant4(uint32_t nib, uint32_t mul, uint32_t add) {
