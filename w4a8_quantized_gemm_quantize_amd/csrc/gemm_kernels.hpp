@@ -118,6 +118,14 @@ __device__ __forceinline__ v4i half_operand(v4i a, int kq, int half) {
     return ((kq >> 1) == half) ? a : v4i{0, 0, 0, 0};
 }
 
+// Weight records streamed once from HBM: 16-byte buffer load with the
+// nontemporal cache policy (cache policy operand 2), as the flat loads of the
+// previous form had (__builtin_nontemporal_load); without it the decode
+// kernels ran 2-7 % slower.
+__device__ __forceinline__ u32x4 buffer_load16_nt(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2);
+}
+
 // ---------------------------------------------------------------- skinny --
 constexpr int kSkinnyMaxVec = 8;    // fused prologue: 16-byte vectors held per thread
 // Wavefronts per workgroup of the fused form: 16 when the weight stream per
@@ -184,28 +192,63 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     // chunk j1 - 1 = nfull - 1, and never uses it.
     const int64_t nfull = k / kChunkK;
     const bool has_half = nfull < nchunks;
-    const int64_t per = (nfull + WAVES - 1) / WAVES;
-    const int64_t j0 = wave * per;
-    const int64_t j1 = (j0 + per < nfull) ? j0 + per : nfull;
+    const int per = (int)((nfull + WAVES - 1) / WAVES);
+    const int j0 = wave * per;
+    const int j1 = (j0 + per < (int)nfull) ? j0 + per : (int)nfull;
     const int8_t *a_q = (const int8_t *)act;
 
+    // Buffer resources over this workgroup's weight tiles and their group
+    // parameters (tiles past n read zero: they only reach unstored outputs)
+    // and, without the fused prologue, over the m rows of activation codes.
+    // Per-lane offsets are fixed for the whole K loop and the chunk goes in
+    // the scalar offset, so the loads need no vector address arithmetic.  The
+    // group parameter comes as the aligned 32-bit word that holds it and the
+    // rebuild constants are taken out of it with one v_perm_b32 and one
+    // v_pk_mad_u16 (device_common.hpp: wparam_consts).  All offsets fit 32
+    // bits: k <= K_MAX, m <= 64.
+    constexpr int kWTileMul = WF == kW8 ? 16 : 8;                // weight bytes per tile = mul * k
+    constexpr int kPSize = WF == kW4Lqq ? 2 : 1;                 // bytes per group parameter
+    const int wtile = kWTileMul * (int)k;
+    const int ptile = kNTile * (int)G * kPSize;
+    const int tiles_here = (int)(ntiles - t0 < NT ? ntiles - t0 : NT);
+    const __amdgpu_buffer_rsrc_t rw =
+        buffer_rsrc(w_packed + t0 * (int64_t)wtile, (uint32_t)tiles_here * wtile);
+    const __amdgpu_buffer_rsrc_t rp =
+        WF == kW8 ? rw : buffer_rsrc(grp_scale + t0 * (int64_t)ptile, (uint32_t)tiles_here * ptile);
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(act, FUSED ? 16u : (uint32_t)(m * k));
+    const WParamSel psel = wparam_selectors<WF>(c);
+    const int poff_c = WF == kW4Lqq ? (c & ~1) * 2 : (c & ~3);
+    int aoff[FUSED ? 1 : MT];                    // activation row offsets (rows past m: row m - 1)
+#pragma unroll
+    for (int mt = 0; mt < (FUSED ? 1 : MT); ++mt) {
+        const int row = (mt * 16 + c < m) ? mt * 16 + c : m - 1;
+        aoff[mt] = row * (int)k + kq * 16;
+    }
+
     // Weights (+ non-fused activation fragments) of D chunks, requested together.
-    // Every load is unconditional: addresses of chunks past the wavefront's range,
-    // tiles past n and rows past m are clamped to valid ones, and what they fetch
-    // is never used (chunks are skipped, rows masked at use, tiles not stored).
-    // A branch around a load would make the compiler wait for it at the join.
+    // Every load is unconditional: chunks past the wavefront's range and rows
+    // past m are clamped to valid ones, tiles past n read zero, and nothing
+    // they fetch is stored (chunks are skipped, those rows and tiles are not
+    // stored).  A branch around a load would make the compiler wait for it at
+    // the join.
     const int64_t tlast = ntiles - 1;
-    auto load_batch = [&](WeightBatch<WF, NT, D, MT, !FUSED, AB> &b, int64_t jb) {
+    auto load_batch = [&](WeightBatch<WF, NT, D, MT, !FUSED, AB> &b, int jb) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            const int64_t j = (jb + d < j1) ? jb + d : j1 - 1;
+            const int j = (jb + d < j1) ? jb + d : j1 - 1;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                const int64_t t = (t0 + nt < ntiles) ? t0 + nt : tlast;
-                const int64_t pidx = t * kNTile * G + (2 * j) * kNTile + c;
-                b.w[d][nt] = load_wrec<WF>(w_packed, t, j, k, lane);
-                b.s[d][nt][0] = load_wparam<WF>(grp_scale, pidx);
-                b.s[d][nt][1] = load_wparam<WF>(grp_scale, pidx + kNTile);
+                if constexpr (WF == kW8) {
+                    b.w[d][nt].r0 = buffer_load16_nt(rw, nt * wtile + lane * 16, j * (2 * kChunkBytes));
+                    b.w[d][nt].r1 = buffer_load16_nt(rw, nt * wtile + lane * 16,
+                                                  j * (2 * kChunkBytes) + kChunkBytes);
+                    b.s[d][nt][0] = b.s[d][nt][1] = 0u;
+                } else {
+                    b.w[d][nt].r = buffer_load16_nt(rw, nt * wtile + lane * 16, j * kChunkBytes);
+                    const int so = j * (2 * kNTile * kPSize);
+                    b.s[d][nt][0] = buffer_load4(rp, nt * ptile + poff_c, so);
+                    b.s[d][nt][1] = buffer_load4(rp, nt * ptile + poff_c, so + kNTile * kPSize);
+                }
             }
             if constexpr (!FUSED) {
 #pragma unroll
@@ -213,8 +256,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
                         const int row = (mt * 16 + c < m) ? mt * 16 + c : m - 1;
-                        b.a[d][h][mt] = *(const v4i *)(a_q + (int64_t)row * k + j * kChunkK +
-                                                       h * kGroup + kq * 16);
+                        b.a[d][h][mt] = __builtin_bit_cast(
+                            v4i, buffer_load16(ra, aoff[mt], j * kChunkK + h * kGroup));
                         if constexpr (AB > 0) {
                             const int64_t ks = 2 * j + h;                  // 64-wide K step
 #pragma unroll
@@ -344,7 +387,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
                         const v4i av[MT], const SaStep &sa) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const v4i wv = wrec_operand<WF>(rec[nt], h, sv[nt]);
+            uint32_t mul = 0u, add = 0u;
+            if constexpr (WF != kW8) wparam_consts<WF>(sv[nt], psel, mul, add);
+            const v4i wv = wrec_operand_ma<WF>(rec[nt], h, mul, add);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 if constexpr (AB == 0) {
@@ -368,13 +413,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
         }
     };
     SaStep sa_none = {};
-    // Activation fragments of rows mt * 16 + c; rows past m read row m - 1 and
-    // are zeroed here.
-    auto mask_rows = [&](v4i av[MT]) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            if (mt * 16 + c >= m) av[mt] = v4i{0, 0, 0, 0};
-    };
+    // Activation fragments of rows mt * 16 + c; rows past m read row m - 1.
+    // Their products land in accumulator rows that are never stored (the
+    // reduction below stores rows < m only), so they need no masking.
     auto lds_act = [&](v4i av[MT], int64_t kk) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -384,12 +425,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     };
 
     // The chunks of batch b starting at jb (the first `cnt` of its D are used).
-    auto compute_batch = [&](const WeightBatch<WF, NT, D, MT, !FUSED, AB> &b, int64_t jb,
-                             int64_t cnt) {
+    auto compute_batch = [&](const WeightBatch<WF, NT, D, MT, !FUSED, AB> &b, int jb, int cnt) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             if (d >= cnt) break;
-            const int64_t j = jb + d;
+            const int j = jb + d;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 uint32_t sv[NT];
@@ -402,7 +442,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) av[mt] = b.a[d][h][mt];
                 }
-                mask_rows(av);
                 if constexpr (AB > 0) mma_step(b.w[d], h, sv, av, b.sa[d][h]);
                 else mma_step(b.w[d], h, sv, av, sa_none);
             }
@@ -416,7 +455,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     // the scheduler would otherwise sink them to reuse registers, exposing
     // their latency.
     WeightBatch<WF, NT, D, MT, !FUSED, AB> other;
-    int64_t jb = j0;
+    int jb = j0;
     while (true) {
         if (jb + D >= j1) {
             if (jb < j1) compute_batch(cur, jb, j1 - jb);
@@ -445,7 +484,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
         for (int nt = 0; nt < NT; ++nt) {
             const int64_t t = (t0 + nt < ntiles) ? t0 + nt : tlast;
             wp[nt] = load_wrec_half<WF>(w_packed, t, j, k, lane);
-            sv[nt] = load_wparam<WF>(grp_scale, t * kNTile * G + (2 * j) * kNTile + c);
+            sv[nt] = WF == kW8 ? 0u
+                               : buffer_load4(rp, nt * ptile + poff_c,
+                                              (int)(2 * j) * kNTile * kPSize);
         }
         v4i av[MT];
         const int64_t kk = j * kChunkK + kq * 16;
@@ -458,7 +499,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
                 av[mt] = *(const v4i *)(a_q + (int64_t)row * k + kk);
             }
         }
-        mask_rows(av);
         SaStep sa_half = {};
         if constexpr (AB > 0) {
             // blocks of 32 or 64 only: k % 128 == 64 excludes blocks of 128
