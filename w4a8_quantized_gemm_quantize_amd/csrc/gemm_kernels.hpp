@@ -779,6 +779,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
         else if constexpr (S == 1) return wsc1;
         else return wsc2;
     };
+    // With weights in registers (kRegW) each wavefront's tiles are read by this
+    // workgroup only: their records are streamed with the nontemporal policy,
+    // which keeps them from evicting the activation tiles that every column
+    // tile re-reads from L2 (70B FFN-down M = 64, split K: 40.7 -> 35.8 us).
+    // In the LDS-weight form a tile is shared by the workgroups of a column of
+    // tiles, so its records are cached normally.
+    auto wload = [&](int voff, int soff) -> u32x4 {
+        if constexpr (kRegW) return buffer_load16_nt(rw, voff, soff);
+        else return buffer_load16(rw, voff, soff);
+    };
     auto fetch_w = [&](int jreq, auto set_tag) {
         WRec<WF>(&wrec)[TPW] = wrec_of(set_tag);
         uint32_t(&wsc)[TPW][2] = wsc_of(set_tag);
@@ -788,11 +798,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
         for (int i = 0; i < TPW; ++i) {
             if constexpr (WF == kW8) {
                 const int so = j * (2 * kChunkBytes);
-                wrec[i].r0 = buffer_load16(rw, woff[i], so);
-                wrec[i].r1 = buffer_load16(rw, woff[i], wfull ? so + kChunkBytes : so);
+                wrec[i].r0 = wload(woff[i], so);
+                wrec[i].r1 = wload(woff[i], wfull ? so + kChunkBytes : so);
                 wsc[i][0] = wsc[i][1] = 0u;
             } else {
-                wrec[i].r = buffer_load16(rw, wfull ? woff[i] : woff_half[i], j * kChunkBytes);
+                wrec[i].r = wload(wfull ? woff[i] : woff_half[i], j * kChunkBytes);
                 const int so = j * (2 * kNTile * kPSize);
                 wsc[i][0] = buffer_load4(rp, poff[i], so);
                 wsc[i][1] = buffer_load4(rp, poff[i], wfull ? so + kNTile * kPSize : so);
