@@ -104,10 +104,13 @@ def copy_probe_gbps(torch, dev, reps=10):
     return gbps
 
 
-def time_graph(torch, fn, copies, reps):
-    """Capture fn(r, stream) for r in range(copies) into one HIP graph, replay it
+def time_graph(torch, fn, copies, reps, min_calls=20):
+    """Capture fn(r % copies, stream) for r in range(calls) into one HIP graph,
+    with calls the smallest multiple of `copies` that is at least min_calls
+    (so the gap between graph launches is spread over many kernels), replay it
     once untimed, then `reps` times between HIP events on the capture stream.
     Returns the average milliseconds per fn call."""
+    calls = copies * max(1, -(-min_calls // copies))
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -118,8 +121,8 @@ def time_graph(torch, fn, copies, reps):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         s = torch.cuda.current_stream()
-        for r in range(copies):
-            fn(r, s)
+        for r in range(calls):
+            fn(r % copies, s)
     stream = torch.cuda.current_stream()
     g.replay()
     torch.cuda.synchronize()
@@ -130,7 +133,7 @@ def time_graph(torch, fn, copies, reps):
         g.replay()
     e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / (reps * copies)
+    return e0.elapsed_time(e1) / (reps * calls)
 
 
 def n_copies(per_copy_bytes):
@@ -497,7 +500,7 @@ def quantizer_leg(torch, w4a8, inputs, dev, stream, reps=20):
             w4a8.quantize_act_blockwise(xs[r], block, q=qs[r], scales=ss[r], stream=st)
         # graph replays of the two input/output sets in turn, as for the GEMMs
         # (per-call events would add the launch gaps to a 35-40 us kernel)
-        ms = time_graph(torch, quant, 2, reps)
+        ms = time_graph(torch, quant, 2, reps // 4)
         gbps = quantizer_algorithmic_bytes(rows * cols, block) / (ms * 1e-3) / 1e9
         entry = {"kernel_ms": ms, "achieved": gbps, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS}
         # dequantization round trip: q, scales -> fp32 and bf16; MSE against x
