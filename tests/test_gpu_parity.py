@@ -38,10 +38,10 @@ def announce(*what):
     (37, 4096, 256), (37, 4096, 512), (37, 4096, 1024), (11, 2048, 2048), (9, 96, 24),
     (5, 28672, 28672), (3, 40960, 40960), (1, 8, 8), (300, 256, 256),
     (66, 4096, 4096), (7, 8192, 8192), (5, 8200, 8200), (4, 6144, 3072),
-    # few long rows (one 1024-thread workgroup per row, up to 32768 elements),
-    # and one past both limits (512 rows of 28672; 2 rows of 32776)
+    # long rows (one 1024-thread workgroup per row, up to 32768 elements), and
+    # rows just past that limit (32776 elements: the 256-thread form)
     (64, 28672, 28672), (512, 12288, 12288), (513, 8200, 8200), (2, 32768, 32768),
-    (2, 32776, 32776),
+    (2, 32776, 32776), (70, 32776, 32776),
 ])
 def test_quantize_matches_oracle(w4a8, rows, cols, block):
     announce("quantize", rows, cols, block)

@@ -160,12 +160,13 @@ __global__ __launch_bounds__(256) void quant_wide_kernel(const u32x4 *__restrict
     }
 }
 
-// Few long blocks (the per-token scales of a decode batch with long rows, e.g.
-// 64 rows of 28672): one 1024-thread workgroup per block, all 16 wavefronts
-// of a CU's share loading at once, so a short grid still has enough loads in
-// flight (a 256-thread workgroup per row took 4.3 us for 64 x 28672, this
-// form 3.2 us).  Up to 1024 * MAXV vectors in registers; the block maximum is
-// a wavefront reduction, then one over the 16 wavefronts in LDS.
+// Long blocks of up to 1024 * MAXV vectors (per-token rows of 8K-32K
+// elements): one 1024-thread workgroup per block, striding over the blocks.
+// All 16 wavefronts of a workgroup load at once, so even a short grid keeps
+// enough loads in flight: 64 x 28672 took 4.3 us with a 256-thread workgroup
+// per row and takes 3.2 us here; 2048 x 28672: 31.2 -> 29.7 us; 4096 x 16384:
+// 40.6 -> 34.9 us.  The block maximum is a wavefront reduction, then one over
+// the 16 wavefronts in LDS.
 template <int MAXV>
 __global__ __launch_bounds__(1024) void quant_wide1k_kernel(const u32x4 *__restrict__ x,
                                                             int64_t nblocks, int64_t block_vecs,
@@ -286,10 +287,11 @@ hipError_t launch_quantize_act(const uint16_t *x, int64_t rows, int64_t cols, in
                     quant_row_wave_kernel<8><<<grid, 256, 0, stream>>>(xv, nblocks, lpb, qv, scales);
                 else
                     quant_row_wave_kernel<16><<<grid, 256, 0, stream>>>(xv, nblocks, lpb, qv, scales);
-            } else if (nblocks <= 512 && lpb <= 1024 * 4) {
-                // few blocks of up to 32768 elements: one 1024-thread workgroup each
-                quant_wide1k_kernel<4><<<(int)nblocks, 1024, 0, stream>>>(
-                    xv, nblocks, (int64_t)lpb, qv, scales);
+            } else if (lpb <= 1024 * 4) {
+                // blocks of up to 32768 elements: a 1024-thread workgroup each
+                const int grid = (int)(nblocks < 65536 ? nblocks : 65536);
+                quant_wide1k_kernel<4><<<grid, 1024, 0, stream>>>(xv, nblocks, (int64_t)lpb, qv,
+                                                                 scales);
             } else {
                 const int grid = (int)(nblocks < 65536 ? nblocks : 65536);
                 quant_wide_kernel<16><<<grid, 256, 0, stream>>>(xv, nblocks, (int64_t)lpb, qv,
