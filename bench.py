@@ -237,11 +237,13 @@ def mfma_probe_leg(torch, w4a8, dev, stream, reps=10):
 
 
 def measure_workload(torch, w4a8, dev, name, a_bits, w_bits, spec, steps, warmup,
-                     packed=None, probes=None):
+                     packed=None, probes=None, prime=None):
     """One workload: `warmup` untimed steps, then exactly `steps` timed steps, each
     step = w4a8_gemm_bf16act (per-token quantization of A + the W4A8 GEMM) over
     the next of R rotating weight/activation copies (> 512 MB in rotation).
-    Returns the step time, the step throughput and the dominant kernel's roofline."""
+    Returns the step time, the step throughput and the dominant kernel's roofline.
+    `prime` (optional) runs after set-up and graph capture, right before the
+    warmup steps."""
     m, n, k = spec["m"], spec["n"], spec["k"]
     out_dtype = torch.bfloat16 if spec["out"] == "bf16" else torch.float32
     out_bytes = 2 if spec["out"] == "bf16" else 4
@@ -279,33 +281,40 @@ def measure_workload(torch, w4a8, dev, name, a_bits, w_bits, spec, steps, warmup
         else:
             w4a8.w4a8_gemm(a_q, a_s, wps[r], gss[r], css[r], n, out=out, stream=st)
 
-    def capture(fn, count=copies):
+    # One graph holds `per_graph` steps (a multiple of the copy count, at least
+    # 20), cycling through the copies, so the gap between graph launches is
+    # spread over many steps.
+    per_graph = copies * max(1, -(-20 // copies))
+
+    def capture(fn, count=per_graph):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             s = torch.cuda.current_stream()
             for r in range(count):
-                fn(r, s)
+                fn(r % copies, s)
         return g
 
     # Warmup: exactly `warmup` untimed steps.  The first is an eager step on
     # copy 0 (it loads the kernels before graph capture); the others replay
-    # graphs: whole graphs of `copies` steps, then a graph of the first
-    # (count mod copies) steps, captured beforehand.  The timed region replays
-    # exactly `steps` steps the same way.
+    # graphs: whole graphs of `per_graph` steps, then a graph of the first
+    # (count mod per_graph) steps, captured beforehand.  The timed region
+    # replays exactly `steps` steps the same way.
     eager = 1 if warmup >= 1 else 0
     if eager:
         step(0, stream)
         torch.cuda.synchronize()
     g_step = capture(step)
     warm_graph = warmup - eager
-    partial = {r: capture(step, r) for r in {steps % copies, warm_graph % copies} if r}
+    partial = {r: capture(step, r) for r in {steps % per_graph, warm_graph % per_graph} if r}
 
     def run_steps(count):
-        for _ in range(count // copies):
+        for _ in range(count // per_graph):
             g_step.replay()
-        if count % copies:
-            partial[count % copies].replay()
+        if count % per_graph:
+            partial[count % per_graph].replay()
 
+    if prime is not None:
+        prime()
     run_steps(warm_graph)
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
@@ -331,14 +340,14 @@ def measure_workload(torch, w4a8, dev, name, a_bits, w_bits, spec, steps, warmup
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        reps = max(1, steps // copies)
+        reps = max(1, steps // per_graph)
         e0.record(stream)
         for _ in range(reps):
             g_gemm.replay()
         e1.record(stream)
         torch.cuda.synchronize()
-        gemm_ms = e0.elapsed_time(e1) / (reps * copies)
-        gemm_launches = reps * copies
+        gemm_ms = e0.elapsed_time(e1) / (reps * per_graph)
+        gemm_launches = reps * per_graph
 
     ops = 2.0 * m * n * k
     tops = ops / (ms_per_step * 1e-3) / 1e12
@@ -379,7 +388,8 @@ def measure_workload(torch, w4a8, dev, name, a_bits, w_bits, spec, steps, warmup
     res = {"workload": f"{name} W4A8 GEMM M={m} K={k} N={n}, per-token int8 activations "
                        f"(quantized in the call), int4 weights group 64, {spec['out']} out",
            "m": m, "n": n, "k": k, "steps": steps, "warmup": warmup, "ms_per_step": ms_per_step,
-           "value": tops, "unit": "TOPS", "weight_copies_rotated": copies, "roofline": roof}
+           "value": tops, "unit": "TOPS", "weight_copies_rotated": copies,
+           "steps_per_graph": per_graph, "roofline": roof}
     del wps, gss, css, acts, wss, out, g_step, partial
     return res
 
@@ -414,15 +424,21 @@ def main():
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     # Measured references on this GPU: a device copy (HBM) and the MFMA-only loop.
+    # They run inside the headline measurement, after its set-up and graph
+    # capture and right before its warmup steps, so the timed steps start on a
+    # GPU that has just been under load (clocks as in steady use), not on one
+    # that sat idle while the host captured the graphs.
     probes = {}
-    if not args.no_probes:
+
+    def run_probes():
         probes["copy_gbps"] = copy_probe_gbps(torch, dev)
         probes["mfma"] = mfma_probe_leg(torch, w4a8, dev, stream)
         log("probes done")
 
     a_bits, w_bits, spec = inputs.workload_inputs(args.workload, seed=0)
     head = measure_workload(torch, w4a8, dev, args.workload, a_bits, w_bits, spec,
-                            max(1, args.steps), max(0, args.warmup), probes=probes)
+                            max(1, args.steps), max(0, args.warmup), probes=probes,
+                            prime=None if args.no_probes else run_probes)
     log(f"{args.workload}: {head['ms_per_step'] * 1e3:.1f} us/step")
     m, n, k = spec["m"], spec["n"], spec["k"]
     line = {
