@@ -349,10 +349,11 @@ w4a8_status w8a8_gemm_bf16act(const uint16_t *a, const int8_t *w_packed, const f
  *            W4A8_ERR_UNSUPPORTED
  * For each activation block b (k in [b * block, (b + 1) * block)):
  *   P_b[m, n] = sum_{k in b} a_q[m, k] * q[n, k] * s_g[n, k / 64]   (int32, exact)
- * and, in binary32 with one rounding per operation and blocks in increasing
- * order (the order within one block's row of a wavefront's K range; ranges of
- * different wavefronts may be summed in another order):
- *   f = 0;  f = f + P_b * a_scale[m, b]  for each b;   out = f * ch_scale[n].
+ * and, in binary32 with blocks in increasing order (the order within one
+ * block's row of a wavefront's K range; ranges of different wavefronts may be
+ * summed in another order), each block folded by one fused multiply-add (one
+ * rounding):
+ *   f = 0;  f = fma(P_b, a_scale[m, b], f)  for each b;   out = f * ch_scale[n].
  * The error against the exact value is at most about (k / block + 2) * 2^-24
  * times sum_b |a_scale[m, b] * P_b| * ch_scale[n].
  * block must be 32, 64 or 128 (else W4A8_ERR_UNSUPPORTED) and divide k

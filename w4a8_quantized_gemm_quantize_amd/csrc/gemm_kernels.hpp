@@ -86,14 +86,14 @@ __device__ __forceinline__ void store4(void *out, int out_dtype, int64_t row, in
 }
 
 // Per-block activation scales (AB > 0): the int32 partial t of one activation
-// block is folded into the binary32 accumulator as f = f + fl(fl(t) * s), block
-// after block in K order.  |t| < 2^24, so fl(t) is exact.
+// block is folded into the binary32 accumulator as f = fl(fl(t) * s + f), one
+// fused multiply-add (one rounding), block after block in K order.  |t| < 2^24,
+// so fl(t) is exact.  The fold is VALU work on every output of every block
+// (a conversion and an FMA); with the product and the sum rounded separately
+// it was a third more (prefill 4096 x 14336 x 4096, block 128: 441 -> 407 us).
 __device__ __forceinline__ void fold4(f32x4 &f, const v4i t, float s) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float p = (float)t[i] * s;
-        f[i] = f[i] + p;
-    }
+    for (int i = 0; i < 4; ++i) f[i] = __builtin_fmaf((float)t[i], s, f[i]);
 }
 
 // Epilogue of the per-block form: out = f * ch_scale, binary32 or bf16.
@@ -923,11 +923,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
             for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
                 for (int tm = 0; tm < TM; ++tm) {
-                    acc[tn][tm] = mfma16x16x64(wv[tn], av[tm], acc[tn][tm]);
-                    if (h == 1) {
-                        fold4(accf[tn][tm], acc[tn][tm], scur[tm][0]);
-                        acc[tn][tm] = v4i{0, 0, 0, 0};
-                    }
+                    // the block's first K step starts from a zero accumulator
+                    // (inline constant), so no register clearing after the fold
+                    // (prefill, block 128: 407 -> 381 us)
+                    acc[tn][tm] =
+                        mfma16x16x64(wv[tn], av[tm], h == 0 ? v4i{0, 0, 0, 0} : acc[tn][tm]);
+                    if (h == 1) fold4(accf[tn][tm], acc[tn][tm], scur[tm][0]);
                 }
         }
     };
