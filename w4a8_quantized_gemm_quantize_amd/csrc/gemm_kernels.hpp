@@ -682,6 +682,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     const int gk = kfull / kGroup;
     const std::integral_constant<bool, true> full_chunk;
     const std::integral_constant<bool, false> half_chunk;
+    const std::integral_constant<bool, true> steady;      // request offsets known whole
+    const std::integral_constant<bool, false> general;
 
     // Buffer resources over this workgroup's rows of A and tiles of W: rows
     // past m and tiles past n read zero (they only reach unstored outputs), so
@@ -789,11 +791,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
         if constexpr (kRegW) return buffer_load16_nt(rw, voff, soff);
         else return buffer_load16(rw, voff, soff);
     };
-    auto fetch_w = [&](int jreq, auto set_tag) {
+    // steady_tag true: jreq is known to be a full chunk (no clamp, no select).
+    auto fetch_w = [&](int jreq, auto set_tag, auto steady_tag) {
         WRec<WF>(&wrec)[TPW] = wrec_of(set_tag);
         uint32_t(&wsc)[TPW][2] = wsc_of(set_tag);
-        const int j = jreq < nchunks ? jreq : nchunks - 1;
-        const bool wfull = j < nfull;
+        constexpr bool kSteady = decltype(steady_tag)::value;
+        const int j = kSteady || jreq < nchunks ? jreq : nchunks - 1;
+        const bool wfull = kSteady || j < nfull;
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             if constexpr (WF == kW8) {
@@ -979,7 +983,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
         if (nchunks > 0) {
             if (nfull > 0) issue_act(0, stage0, full_chunk);
             else issue_act(0, stage0, half_chunk);
-            fetch_w(0, stage0);
+            fetch_w(0, stage0, general);
             // every request of chunk 0 before any of chunk 1: the wait below
             // counts on that order
             __builtin_amdgcn_sched_barrier(0);
@@ -988,7 +992,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
             const int j1 = nchunks > 1 ? 1 : 0;
             if (j1 < nfull) issue_act(j1, stage1, full_chunk);
             else issue_act(j1, stage1, half_chunk);
-            fetch_w(1, stage1);
+            fetch_w(1, stage1, general);
         }
         __builtin_amdgcn_s_waitcnt(kWaitOlder);
         asm volatile("" ::: "memory");
@@ -996,8 +1000,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
         asm volatile("" ::: "memory");
     } else {
         if (nchunks > 0) {
-            fetch_w(0, stage0);
-            fetch_w(1, stage1);
+            fetch_w(0, stage0, general);
+            fetch_w(1, stage1, general);
             if (nfull > 0) {
                 rebuild_w(stage0, full_chunk);
                 issue_act(0, stage0, full_chunk);
@@ -1015,7 +1019,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
         __builtin_amdgcn_sched_barrier(0);
         if (j + 1 < nfull) issue_act(j + 1, nxt, full_chunk);
         else if (j + 1 < nchunks) issue_act(j + 1, nxt, half_chunk);
-        fetch_w(j + 2, cur);
+        fetch_w(j + 2, cur, general);
         if constexpr (AB > 0)
             if (j + 1 < nchunks) fetch_s(j + 1, snxt);
         __builtin_amdgcn_sched_barrier(0);
@@ -1039,25 +1043,42 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     // a barrier that waits for chunk j + 1's requests only.  Requests past
     // the last chunk are clamped to it (every address stays inside the
     // operands) and land in a stage and set that are not used again.
-    auto iteration_rw = [&](int j, auto cur, auto ahead) {
-        const int ja = j + 2 < nchunks ? j + 2 : nchunks - 1;
-        if (ja < nfull) issue_act(ja, ahead, full_chunk);
-        else issue_act(ja, ahead, half_chunk);
-        fetch_w(j + 2, ahead);
+    //   In the steady state (steady_tag true: chunks j .. j + 2 all whole) the
+    // requests take fixed offsets.  Otherwise the clamp and the whole / half
+    // choice are selects, whose results the register allocator may place in
+    // a register set that a load still in flight will write; the compiler
+    // then waits for that load before the select, which had cut the requests
+    // in flight to one chunk in every third iteration.
+    auto iteration_rw = [&](int j, auto cur, auto ahead, auto steady_tag) {
+        if constexpr (decltype(steady_tag)::value) {
+            issue_act(j + 2, ahead, full_chunk);
+            fetch_w(j + 2, ahead, steady_tag);
+        } else {
+            const int ja = j + 2 < nchunks ? j + 2 : nchunks - 1;
+            if (ja < nfull) issue_act(ja, ahead, full_chunk);
+            else issue_act(ja, ahead, half_chunk);
+            fetch_w(j + 2, ahead, steady_tag);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        if (j >= nfull) half_records(cur);
+        if (!decltype(steady_tag)::value && j >= nfull) half_records(cur);
         mma_step(cur, 0);
-        if (j < nfull) mma_step(cur, 1);
+        if (decltype(steady_tag)::value || j < nfull) mma_step(cur, 1);
         __builtin_amdgcn_s_waitcnt(kWaitOlder);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     };
     if constexpr (kRegW) {
-        for (int j = 0; j < nchunks; j += 3) {
-            iteration_rw(j, stage0, stage2);
-            if (j + 1 < nchunks) iteration_rw(j + 1, stage1, stage0);
-            if (j + 2 < nchunks) iteration_rw(j + 2, stage2, stage1);
+        int j = 0;
+        for (; j + 4 < nfull; j += 3) {
+            iteration_rw(j, stage0, stage2, steady);
+            iteration_rw(j + 1, stage1, stage0, steady);
+            iteration_rw(j + 2, stage2, stage1, steady);
+        }
+        for (; j < nchunks; j += 3) {
+            iteration_rw(j, stage0, stage2, general);
+            if (j + 1 < nchunks) iteration_rw(j + 1, stage1, stage0, general);
+            if (j + 2 < nchunks) iteration_rw(j + 2, stage2, stage1, general);
         }
     } else {
         for (int j = 0; j < nchunks; j += 2) {
