@@ -209,10 +209,13 @@ def cpu_baseline(a_bits, w_bits, spec, seconds):
             }}
 
 
-def mfma_probe_leg(torch, w4a8, dev, stream, reps=10):
+def mfma_probe_leg(torch, w4a8, dev, stream, reps=40):
     """The int8 matrix-core reference (MFMA-only loop built with the library): one
     workgroup of 8 wavefronts per compute unit, timed with HIP events on the
-    launch stream; the shader clock is read inside the kernel."""
+    launch stream; the shader clock is read inside the kernel.  About 40 ms of
+    launches: a GPU coming out of idle takes some 30 ms of sustained load to
+    reach its steady clock, and this leg runs right before the headline's
+    warmup steps."""
     ncu = torch.cuda.get_device_properties(dev).multi_processor_count
     iters = 4096
     for _ in range(3):
