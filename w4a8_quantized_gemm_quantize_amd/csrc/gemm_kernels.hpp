@@ -597,13 +597,14 @@ __device__ __forceinline__ int act_lds_off(int row, int c16) {
 // kslice (a multiple of 128): blockIdx.y = s takes K range [s kslice, (s + 1)
 // kslice) and writes its int32 partial sums (out_dtype 2) to slice s of `out`,
 // [gridDim.y][m][ldo]; one slice (kslice >= k) is the whole product.  Per-token
-// scales only when split.
+// scales only when split.  first_wave: workgroups the device starts before the
+// rest (one per CU); with two per CU the later one of each pair is second.
 template <int WF, int BM, int BN, int WAVES_M, int WAVES_N, int AB = 0>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 : 1) void gemm_tiled_kernel(
     const int8_t *__restrict__ a_q, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ w_packed, const uint8_t *__restrict__ grp_scale,
     const float *__restrict__ ch_scale, int64_t m, int64_t n, int64_t k,
-    void *__restrict__ out, int64_t ldo, int out_dtype, int64_t kslice) {
+    void *__restrict__ out, int64_t ldo, int out_dtype, int64_t kslice, int64_t first_wave) {
     using L = TiledLds<BM, BN>;
     constexpr int WAVES = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -1049,7 +1050,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
     // a register set that a load still in flight will write; the compiler
     // then waits for that load before the select, which had cut the requests
     // in flight to one chunk in every third iteration.
+    //   Two workgroups share each CU in the split-K launch, and the issue
+    // arbiter favours the older wavefronts: the first-started workgroup of a
+    // pair ran its K loop in 17.4-18.0 us, the second in 21.8-22.3 us (70B
+    // FFN-down M = 64, per-workgroup stamps).  The pair takes turns at a
+    // raised wave priority, chunk by chunk, so both progress together (two
+    // boxes, interleaved: fused M = 64 39.9-40.4 -> 39.3-39.4 us, split GEMM
+    // M = 64 36.3 -> 35.5 us, M = 32 30.8-31.2 -> 29.9-30.5 us).
+    const bool second =
+        (int64_t)blockIdx.x + (int64_t)blockIdx.y * gridDim.x >= first_wave;
     auto iteration_rw = [&](int j, auto cur, auto ahead, auto steady_tag) {
+        if ((j + (int)second) & 1) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
         if constexpr (decltype(steady_tag)::value) {
             issue_act(j + 2, ahead, full_chunk);
             fetch_w(j + 2, ahead, steady_tag);
@@ -1080,6 +1092,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, AB == 64 || AB == 128 ? 2 :
             if (j + 1 < nchunks) iteration_rw(j + 1, stage1, stage0, general);
             if (j + 2 < nchunks) iteration_rw(j + 2, stage2, stage1, general);
         }
+        __builtin_amdgcn_s_setprio(0);
     } else {
         for (int j = 0; j < nchunks; j += 2) {
             iteration(j, stage0, stage1);
@@ -1227,7 +1240,7 @@ void launch_tiled_cols(const int8_t *a_q, const float *a_scale, const uint8_t *w
                                                           64 * WAVES_M * WAVES_N, 0, stream>>>(
         a_q, a_scale, w_packed + t_off * wtile,
         grp_scale ? grp_scale + t_off * ptile : grp_scale, ch_scale + n_off, m, n_sub, k,
-        (uint8_t *)out + n_off * esize, ldo, out_dtype, kslice);
+        (uint8_t *)out + n_off * esize, ldo, out_dtype, kslice, (int64_t)device_cu_count());
 }
 
 // ------------------------------------------------------------- split K --
