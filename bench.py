@@ -262,8 +262,8 @@ def measure_workload(torch, w4a8, dev, name, a_bits, w_bits, spec, steps, warmup
     gss = [gs0] + [gs0.clone() for _ in range(copies - 1)]
     css = [cs0] + [cs0.clone() for _ in range(copies - 1)]
     acts = [a0] + [a0.clone() for _ in range(copies - 1)]
-    # codes and scales of the quantized activations, then (16 < m <= 64, large K)
-    # the int32 partial sums of the split-K GEMM
+    # codes and scales of the quantized activations, then (decode batches at
+    # large K) the int32 partial sums of the split-K GEMM
     ws_base = w4a8.workspace_bytes(m, k)
     split = w4a8.gemm_workspace_bytes(m, n, k) > 0
     wss = [torch.empty(w4a8.workspace_bytes(m, k, n), dtype=torch.uint8, device=dev)

@@ -151,11 +151,14 @@ def test_bf16act_workspace_and_validation(lib):
 
 
 def splitk_bytes_expected(m, n, k):
-    """Split-K scratch size restated from its definition: for 16 < m <= 64 and at
-    least two whole 128-wide chunks, S = min(ceil(512 / ceil(n / 128)), k // 128,
-    16) slices of whole chunks, split only if S >= 2 and 32 S m <= k; one int32
-    [m, n] slice per slice of K actually used."""
-    if m <= 16 or m > 64 or k < 256:
+    """Split-K scratch size restated from its definition: for 16 < m <= 64, or 5 <=
+    m <= 16 with m k >= 8 * 28672, and at least two whole 128-wide chunks, S =
+    min(ceil(512 / ceil(n / 128)), k // 128, 16) slices of whole chunks, split
+    only if S >= 2 and 32 S m <= k; one int32 [m, n] slice per slice of K
+    actually used."""
+    if m < 5 or m > 64 or k < 256:
+        return 0
+    if m <= 16 and m * k < 8 * 28672:
         return 0
     ntb = -(-n // 128)
     s = min(-(-512 // ntb), k // 128, 16)
@@ -179,6 +182,9 @@ def test_gemm_ws_workspace_and_validation(lib):
     assert ws(20, 16384, 2624) == 5 * 20 * 16384 * 4      # 4 x 5 chunks + a half-chunk slice
     assert ws(17, 256, 10304) == 17 * 17 * 256 * 4        # 16 x 5 chunks + a half-chunk slice
     assert ws(48, 8192, 8192) == 0                        # partials would outweigh the gain
+    assert ws(16, 8192, 28672) == 8 * 16 * 8192 * 4       # a decode batch at large K
+    assert ws(16, 8192, 12288) == 0                       # m k below 8 * 28672
+    assert ws(4, 8192, 65536) == 0                        # m < 5 never splits
     assert ws(64, 8192, 4096) == 0
     # the rule over seeded random shapes around its edges (m range, half chunks,
     # the 16-slice cap, the 32 S m <= k cut)

@@ -162,7 +162,7 @@ def test_gemm_int32_accumulator_bit_exact(w4a8, m, n, k):
     assert np.array_equal(acc.cpu().numpy(), acc_ref)
 
 
-# Split K (16 < m <= 64 with a workspace): the K slices, their int32 partials and
+# Split K (decode batches with a workspace): the K slices, their int32 partials and
 # the summing pass must reproduce the one-pass result exactly.
 SPLITK_SHAPES = [
     (20, 16384, 2624),  # 4 slices of 5 chunks and a fifth of the trailing half chunk only
@@ -172,6 +172,8 @@ SPLITK_SHAPES = [
     (64, 8192, 28672),  # 70B-like FFN down, M = 64: 8 slices
     (64, 28672, 8192),  # 70B-like FFN up shape, M = 64: 3 slices
     (17, 256, 10304),   # 16 slices of 5 chunks plus a 17th of the trailing half chunk
+    (12, 8192, 28672),  # a decode batch below the 64-row tile: rows past m read zeros
+    (16, 4096, 14336),  # m k exactly at the small-batch threshold, 16 slices
 ]
 
 
@@ -209,11 +211,11 @@ def test_gemm_splitk_equals_one_pass(w4a8, m, n, k):
                            y2.view(torch.int32) if dt != torch.bfloat16 else y2.view(torch.int16))
 
 
+@pytest.mark.parametrize("m,n,k", [(24, 14352, 4096), (16, 8192, 14336)])
 @pytest.mark.parametrize("fmt", ["w4", "lqq", "w8"])
-def test_fused_splitk_workspace_equals_without(w4a8, fmt):
+def test_fused_splitk_workspace_equals_without(w4a8, fmt, m, n, k):
     """The fused entry points split K when the workspace has room for the partials;
     the result, and the codes and scales left in the workspace, do not change."""
-    m, n, k = 24, 14352, 4096
     announce("fused split-K", fmt, m, n, k)
     w = to_dev_bf16(inputs.weights(n, k, seed=17))
     a = to_dev_bf16(inputs.activations(m, k, seed=19, outlier_frac=0.001))
@@ -396,8 +398,8 @@ def _sampled_check(w4a8, name, n_rows=48, n_cols=96, seed=0):
     announce("workload", name, m, n, k)
     wp, gs, cs = w4a8.pack_w4_grouped(to_dev_bf16(w))
     ad = to_dev_bf16(a)
-    # the workspace bench.py gives the step: codes, scales and (16 < m <= 64,
-    # large K) room for the split-K partials
+    # the workspace bench.py gives the step: codes, scales and (decode batches
+    # at large K) room for the split-K partials
     ws = torch.empty(w4a8.workspace_bytes(m, k, n), dtype=torch.uint8, device="cuda")
     y = w4a8.w4a8_gemm_bf16act(ad, wp, gs, cs, n, out_dtype=torch.bfloat16, workspace=ws)
     acc = w4a8.w4a8_gemm_bf16act(ad, wp, gs, cs, n, out_dtype=torch.int32)

@@ -158,7 +158,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     const uint8_t *__restrict__ w_packed, const uint8_t *__restrict__ grp_scale,
     const float *__restrict__ ch_scale, int m, int64_t n, int64_t k,
     void *__restrict__ out, int out_dtype, int8_t *__restrict__ ws_q,
-    float *__restrict__ ws_s) {
+    float *__restrict__ ws_s, int64_t first_wave) {
     constexpr int THREADS = 64 * WAVES;
     constexpr int ROWS = MT * 16;
     extern __shared__ __attribute__((aligned(16))) uint8_t act_lds[];  // FUSED: [m][k + 16]
@@ -454,13 +454,22 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     // both).  The scheduling barriers keep the requests ahead of the uses:
     // the scheduler would otherwise sink them to reuse registers, exposing
     // their latency.
+    //   With more workgroups than CUs, two share a CU and the issue arbiter
+    // favours the older one's wavefronts; the two take turns at a raised
+    // wave priority, batch by batch, so they stream their weights together
+    // rather than one after the other (same boxes, interleaved: ffn-down
+    // M = 16 41.5 -> 39.5 us, M = 1 22.8 -> 22.6 us; one workgroup per CU
+    // unchanged).
     WeightBatch<WF, NT, D, MT, !FUSED, AB> other;
     int jb = j0;
+    const bool second = (int64_t)blockIdx.x >= first_wave;
     while (true) {
         if (jb + D >= j1) {
             if (jb < j1) compute_batch(cur, jb, j1 - jb);
             break;
         }
+        if (second) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
         load_batch(other, jb + D);
         __builtin_amdgcn_sched_barrier(0);
         compute_batch(cur, jb, D);
@@ -469,11 +478,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
             compute_batch(other, jb, j1 - jb);
             break;
         }
+        if (second) __builtin_amdgcn_s_setprio(0);
+        else __builtin_amdgcn_s_setprio(1);
         load_batch(cur, jb + D);
         __builtin_amdgcn_sched_barrier(0);
         compute_batch(other, jb, D);
         jb += D;
     }
+    __builtin_amdgcn_s_setprio(0);
 
     if (has_half && wave == WAVES - 1) {
         // Trailing 64-wide chunk: one K step.
@@ -1216,7 +1228,8 @@ void launch_skinny(const void *act, const float *a_scale, const uint8_t *w_packe
     const unsigned grid = (unsigned)((ntiles + NT - 1) / NT);
     gemm_skinny_kernel<WF, MT, NT, WAVES, D, FUSED, AV, AB, KF><<<grid, 64 * WAVES, dyn_lds,
                                                             stream>>>(
-        act, a_scale, w_packed, grp_scale, ch_scale, (int)m, n, k, out, out_dtype, ws_q, ws_s);
+        act, a_scale, w_packed, grp_scale, ch_scale, (int)m, n, k, out, out_dtype, ws_q, ws_s,
+        (int64_t)device_cu_count());
 }
 
 // Output columns [n_off, n_off + n_sub) of an [m, ldo] product: the weight
@@ -1247,21 +1260,30 @@ void launch_tiled_cols(const int8_t *a_q, const float *a_scale, const uint8_t *w
 // The skinny kernel's wavefronts split K inside one workgroup per 16-channel
 // tile, so every workgroup reads all of A: at m = 64, k = 28672 that is 470 MB
 // of activation loads for 117 MB of weights, and the vector-memory address
-// path of the CUs, not HBM, sets the time.  With a caller workspace, 16 < m <=
-// 64 instead runs 64 x 128 output tiles of the tiled kernel (A shared by its 8
-// wavefronts through LDS) over S slices of K, each slice writing int32
-// partials, then a pass that sums the slices (exact, any order) and applies
-// the same binary32 epilogue as the one-pass kernels.
+// path of the CUs, not HBM, sets the time.  With a caller workspace, such
+// shapes instead run 64 x 128 output tiles of the tiled kernel (A shared by its
+// 8 wavefronts through LDS; rows past m read zero) over S slices of K, each
+// slice writing int32 partials, then a pass that sums the slices (exact, any
+// order) and applies the same binary32 epilogue as the one-pass kernels.
 constexpr int kSplitBM = 64, kSplitBN = 128;
+// Smallest m * k at which a batch of 5..16 rows splits.  Fused bf16 calls, n =
+// 8192, same boxes: m = 16, k = 28672 41.4 -> 33.6 us; m = 12 37.1 -> 31.8; m = 8
+// 32.9 -> 31.3; m = 16, k = 14336 26.5 -> 24.4; below it the split lost (m = 16,
+// k = 12288 21.7 -> 22.1; m = 8, k = 16384 21.8 -> 24.0; m = 5, k = 28672 29.8 ->
+// 30.7).
+constexpr int64_t kSplitSmallMK = 8 * 28672;
 
-// Slices of K for an m x n x k split-K product (0: not split).  About 512
+// Slices of K for an m x n x k split-K product (0: not split): 16 < m <= 64,
+// or 5 <= m <= 16 with m k >= kSplitSmallMK (the rows of a 64-row tile past m
+// cost MFMA work but no memory traffic).  About 512
 // workgroups (two per CU: one alone leaves too few loads in flight), at most
 // 16 slices of at least one chunk.  The partials cost 8 S m n bytes (written,
 // then read) against n k / 2 bytes of 4-bit weights, so K is split only while
 // that stays within half the weights (32 S m <= k); below it the one-pass
 // kernel is faster (e.g. m = 48, n = k = 8192).
 inline int64_t splitk_slices(int64_t m, int64_t n, int64_t k) {
-    if (m <= 16 || m > 64 || k < 2 * kChunkK) return 0;
+    if (m < 5 || m > 64 || k < 2 * kChunkK) return 0;
+    if (m <= 16 && m * k < kSplitSmallMK) return 0;
     const int64_t ntb = (n + kSplitBN - 1) / kSplitBN;
     int64_t s = (512 + ntb - 1) / ntb;
     const int64_t nfull = k / kChunkK;
