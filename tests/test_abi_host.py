@@ -151,19 +151,28 @@ def test_bf16act_workspace_and_validation(lib):
 
 
 def splitk_bytes_expected(m, n, k):
-    """Split-K scratch size restated from its definition: for 16 < m <= 64, or 5 <=
-    m <= 16 with m k >= 8 * 28672, and at least two whole 128-wide chunks, S =
-    min(ceil(512 / ceil(n / 128)), k // 128, 16) slices of whole chunks, split
-    only if S >= 2 and 32 S m <= k; one int32 [m, n] slice per slice of K
-    actually used."""
-    if m < 5 or m > 64 or k < 256:
+    """Split-K scratch size restated from its definition, for at least two whole
+    128-wide chunks:
+    - 16 < m <= 64, or 5 <= m <= 16 with m k >= 8 * 28672: S = min(ceil(512 /
+      ceil(n / 128)), k // 128, 16) slices of whole chunks, split only if S >= 2
+      and 32 S m <= k;
+    - m > 64: S = min(256 // (ceil(m / 128) ceil(n / 256)), k // (8 m), k // 128,
+      16), split only if S >= 2;
+    one int32 [m, n] slice per slice of K actually used."""
+    if m < 5 or k < 256:
         return 0
     if m <= 16 and m * k < 8 * 28672:
         return 0
-    ntb = -(-n // 128)
-    s = min(-(-512 // ntb), k // 128, 16)
-    if s < 2 or 32 * s * m > k:
-        return 0
+    if m > 64:
+        tiles = -(-m // 128) * -(-n // 256)
+        s = min(256 // tiles, k // (8 * m), k // 128, 16)
+        if s < 2:
+            return 0
+    else:
+        ntb = -(-n // 128)
+        s = min(-(-512 // ntb), k // 128, 16)
+        if s < 2 or 32 * s * m > k:
+            return 0
     kslice = -(-(k // 128) // s) * 128
     return -(-k // kslice) * m * n * 4
 
@@ -185,12 +194,16 @@ def test_gemm_ws_workspace_and_validation(lib):
     assert ws(16, 8192, 28672) == 8 * 16 * 8192 * 4       # a decode batch at large K
     assert ws(16, 8192, 12288) == 0                       # m k below 8 * 28672
     assert ws(4, 8192, 65536) == 0                        # m < 5 never splits
+    assert ws(128, 8192, 28672) == 8 * 128 * 8192 * 4     # 32 tiles of 128 x 256: 8 slices
+    assert ws(512, 8192, 28672) == 2 * 512 * 8192 * 4
+    assert ws(1024, 8192, 28672) == 0                     # 256 tiles fill the CUs
+    assert ws(4096, 14336, 4096) == 0
     assert ws(64, 8192, 4096) == 0
     # the rule over seeded random shapes around its edges (m range, half chunks,
     # the 16-slice cap, the 32 S m <= k cut)
     rng = np.random.default_rng(7)
     for _ in range(2000):
-        m = int(rng.integers(0, 80))
+        m = int(rng.integers(0, 80)) if rng.random() < 0.6 else int(rng.integers(64, 1100))
         n = 16 * int(rng.integers(1, 2400))
         k = 64 * int(rng.integers(1, 600))
         assert ws(m, n, k) == splitk_bytes_expected(m, n, k), (m, n, k)

@@ -174,6 +174,9 @@ SPLITK_SHAPES = [
     (17, 256, 10304),   # 16 slices of 5 chunks plus a 17th of the trailing half chunk
     (12, 8192, 28672),  # a decode batch below the 64-row tile: rows past m read zeros
     (16, 4096, 14336),  # m k exactly at the small-batch threshold, 16 slices
+    (96, 8192, 4096),   # 128 x 256 tiles (m > 64), 5 slices, rows past m read zeros
+    (200, 2048, 16384), # 128 x 256 tiles, two row tiles (ragged), 10 slices
+    (129, 4160, 8256),  # ragged M and N, 7 slices, the last ending on a half chunk
 ]
 
 

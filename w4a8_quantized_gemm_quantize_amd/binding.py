@@ -265,8 +265,9 @@ def gemm_workspace_bytes(m: int, n: int, k: int) -> int:
 def w4a8_gemm_ws(a_q, a_scale, w_packed, grp_scale, ch_scale, n: int,
                  out_dtype=torch.bfloat16, group: int = GROUP, out=None, workspace=None,
                  stream=None):
-    """w4a8_gemm with a caller workspace that lets decode batches (5 <= m <= 64, large
-    K) split K (same result)."""
+    """w4a8_gemm with a caller workspace that lets batches whose output tiles would
+    not fill the GPU (5 <= m <= 64 at large K, or m > 64 with few tiles) split K
+    (same result)."""
     _dev(a_q, torch.int8, "a_q")
     m, k = a_q.shape
     if out is None:
@@ -287,7 +288,8 @@ def w4a8_gemm_ws(a_q, a_scale, w_packed, grp_scale, ch_scale, n: int,
 
 def workspace_bytes(m: int, k: int, n: int = None) -> int:
     """Workspace of the fused entry points: codes and scales, plus (given n) the
-    split-K partials that let decode batches (5 <= m <= 64, large K) split K."""
+    split-K partials that let batches whose output tiles would not fill the GPU
+    split K."""
     base = int(_lib.w4a8_gemm_bf16act_workspace_bytes(m, k))
     return base + (gemm_workspace_bytes(m, n, k) if n is not None else 0)
 

@@ -1272,21 +1272,42 @@ constexpr int kSplitBM = 64, kSplitBN = 128;
 // k = 12288 21.7 -> 22.1; m = 8, k = 16384 21.8 -> 24.0; m = 5, k = 28672 29.8 ->
 // 30.7).
 constexpr int64_t kSplitSmallMK = 8 * 28672;
+// Batches of 65 rows and more whose 128 x 256 tiles number fewer than the
+// CUs: the one-pass kernels leave CUs idle (8192 x 28672, same box: m = 128 222
+// us, m = 256 182 us, against 36 us at m = 64 split), so K is split over
+// 128 x 256 tiles (the weights-in-registers form, one workgroup per CU).
+constexpr int kSplitMidBM = 128, kSplitMidBN = 256;
+constexpr int64_t kSplitMidWgs = 256;
 
-// Slices of K for an m x n x k split-K product (0: not split): 16 < m <= 64,
-// or 5 <= m <= 16 with m k >= kSplitSmallMK (the rows of a 64-row tile past m
-// cost MFMA work but no memory traffic).  About 512
-// workgroups (two per CU: one alone leaves too few loads in flight), at most
-// 16 slices of at least one chunk.  The partials cost 8 S m n bytes (written,
-// then read) against n k / 2 bytes of 4-bit weights, so K is split only while
-// that stays within half the weights (32 S m <= k); below it the one-pass
-// kernel is faster (e.g. m = 48, n = k = 8192).
+// Slices of K for an m x n x k split-K product (0: not split).  Up to 64 rows
+// (16 < m <= 64, or 5 <= m <= 16 with m k >= kSplitSmallMK; the rows of a
+// 64-row tile past m cost MFMA work but no memory traffic): 64 x 128 tiles,
+// about 512 workgroups (two per CU: one alone leaves too few loads in flight),
+// at most 16 slices of at least one chunk.  The partials cost 8 S m n bytes
+// (written, then read) against n k / 2 bytes of 4-bit weights, so K is split
+// only while that stays within half the weights (32 S m <= k); below it the
+// one-pass kernel is faster (e.g. m = 48, n = k = 8192).  More rows: the
+// 128 x 256 form below.
 inline int64_t splitk_slices(int64_t m, int64_t n, int64_t k) {
-    if (m < 5 || m > 64 || k < 2 * kChunkK) return 0;
+    if (m < 5 || k < 2 * kChunkK) return 0;
     if (m <= 16 && m * k < kSplitSmallMK) return 0;
+    const int64_t nfull = k / kChunkK;
+    if (m > 64) {
+        // 128 x 256 tiles with weights in registers (one workgroup per CU):
+        // split while the tiles alone would leave CUs idle, into at most one
+        // round of kSplitMidWgs workgroups, with the partials within twice
+        // the weight bytes (8 S m n <= n k): idle CUs cost more than that
+        // traffic at these sizes
+        const int64_t tiles = ((m + kSplitMidBM - 1) / kSplitMidBM) *
+                              ((n + kSplitMidBN - 1) / kSplitMidBN);
+        int64_t s = kSplitMidWgs / tiles;
+        if (s > k / (8 * m)) s = k / (8 * m);
+        if (s > nfull) s = nfull;
+        if (s > 16) s = 16;
+        return s >= 2 ? s : 0;
+    }
     const int64_t ntb = (n + kSplitBN - 1) / kSplitBN;
     int64_t s = (512 + ntb - 1) / ntb;
-    const int64_t nfull = k / kChunkK;
     if (s > nfull) s = nfull;
     if (s > 16) s = 16;
     if (s < 2 || 32 * s * m > k) return 0;
@@ -1365,8 +1386,14 @@ void launch_splitk(const int8_t *a_q, const float *a_scale, const uint8_t *w_pac
     const int64_t s = splitk_slices(m, n, k);
     const int64_t kslice = splitk_kslice(k, s);
     const int slices = (int)((k + kslice - 1) / kslice);
-    launch_tiled_cols<WF, kSplitBM, kSplitBN, 1, 8>(a_q, a_scale, w_packed, grp_scale, ch_scale, m,
-                                                    0, n, n, k, partials, 2, stream, kslice);
+    if (m > kSplitBM)
+        launch_tiled_cols<WF, kSplitMidBM, kSplitMidBN, 1, 8>(a_q, a_scale, w_packed, grp_scale,
+                                                              ch_scale, m, 0, n, n, k, partials, 2,
+                                                              stream, kslice);
+    else
+        launch_tiled_cols<WF, kSplitBM, kSplitBN, 1, 8>(a_q, a_scale, w_packed, grp_scale,
+                                                        ch_scale, m, 0, n, n, k, partials, 2,
+                                                        stream, kslice);
     const int64_t quads = m * (n / 4);
     int64_t grid = (quads + 255) / 256;
     if (grid > 4096) grid = 4096;

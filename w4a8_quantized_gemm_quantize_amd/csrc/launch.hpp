@@ -21,8 +21,8 @@ hipError_t launch_unpack_w4(const uint8_t *w_packed, const uint8_t *grp_scale, i
                             int64_t k, int8_t *q, uint8_t *s_g, hipStream_t stream);
 // out_dtype: 0 = binary32, 1 = bf16, 2 = int32 accumulator.
 // partials (optional, splitk_partial_bytes(m, n, k) bytes, 16-byte aligned):
-// int32 scratch that lets 5 <= m <= 64 split K over workgroups (splitk_slices:
-// m > 16, or m k >= 8 * 28672); without it those
+// int32 scratch that lets batches whose output tiles would not fill the GPU
+// split K over workgroups (splitk_slices); without it those
 // shapes run the one-pass skinny kernel.  Same result bit for bit either way.
 size_t splitk_partial_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_w4a8_gemm(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
