@@ -174,11 +174,15 @@ w4a8_status w4a8_gemm(const int8_t *a_q, const float *a_scale, const uint8_t *w_
  * Bytes of optional scratch that lets w4a8_gemm_ws (and the fused entry points
  * below) split K over workgroups for an m x n x k product: int32 partial sums,
  * (S slices of m * n int32, S from 2 to 16).  Split shapes:
- *   - 16 < m <= 64, and 5 <= m <= 16 when m * k >= 229376 (decode batches whose
- *     one-pass kernel re-reads all of A in every workgroup), while the
- *     partials stay within half the weight bytes (32 * S * m <= k);
+ *   - 5 <= m <= 64 (the one-pass kernel re-reads all of A in every
+ *     workgroup): S = min(ceil(512 / ceil(n / 128)), 16), cut to keep the
+ *     partials within half the weight bytes (32 * S * m <= k); for m > 16
+ *     with no cut always split, otherwise where a model of the two paths'
+ *     times, fitted to MI355X measurements, favours the split;
  *   - m > 64 with at most 128 output tiles of 128 x 256 (the one-pass kernels
- *     would leave CUs idle), S = min(256 / tiles, k / (8 m)).
+ *     would leave CUs idle), S = min(256 / tiles, k / (8 m)), or up to
+ *     64 MiB of partials when k >= 4096 (k >= 2048 with at most 32 tiles),
+ *     with slices of at least four 128-wide chunks.
  * 0 when the shape is not split (also for fewer than two 128-wide chunks of
  * K).  Part of the GEMM design choices, not of the method: the
  * result is the same bit for bit.
@@ -232,10 +236,12 @@ w4a8_status w4a8_gemm_bf16act(const uint16_t *a, const uint8_t *w_packed,
  * the inputs and `out` as usual.
  *   - The array holds W4A8_NOALLOC_SCRATCH_BYTES (64 MiB) per device, placed
  *     when the library's code is loaded on that device and kept until the
- *     process ends.  A call whose workspace would exceed it,
- *     w4a8_gemm_bf16act_workspace_bytes(m, k) + w4a8_gemm_workspace_bytes(m,
- *     n, k) > W4A8_NOALLOC_SCRATCH_BYTES, returns W4A8_ERR_UNSUPPORTED before
- *     touching the device (the 70B FFN-down shapes up to m = 2048 fit).
+ *     process ends.  A call whose activation codes and scales would exceed
+ *     it, w4a8_gemm_bf16act_workspace_bytes(m, k) >
+ *     W4A8_NOALLOC_SCRATCH_BYTES, returns W4A8_ERR_UNSUPPORTED before
+ *     touching the device (the 70B FFN-down shapes up to m = 2048 fit).  When
+ *     the codes fit but the split-K partials, w4a8_gemm_workspace_bytes(m, n,
+ *     k) more, do not, K is not split (same result bit for bit).
  *   - Every call on a device shares that device's array and leaves its
  *     contents behind: calls that overlap on one device (two streams, two
  *     host threads) race and must be ordered by the caller.

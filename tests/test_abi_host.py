@@ -150,30 +150,53 @@ def test_bf16act_workspace_and_validation(lib):
     assert f(A, B, C, D, 8, 64, 4096, 32, E, 1, A, need, NUL) == ERR_UNSUPPORTED
 
 
+def splitk_small_pays(m, n, k, s):
+    """The modelled times of the two small-batch paths, restated in exact
+    integers (ns scaled by 256 and by 1000): split when
+    (7400 + 360 C max(256, G) / 256) < 0.9 (1500 + R k (300 + 28 m) / 1000)
+    with C chunks per slice, G = S ceil(n / 128) split workgroups and R rounds
+    of 256 one-pass workgroups (one 16-channel tile each, two for m > 32 with
+    at least 512 tiles)."""
+    chunks = -(-(k // 128) // s)
+    wgs = -(-n // 128) * s
+    t_split = 7400 * 256 + 360 * chunks * max(wgs, 256)
+    tiles = n // 16
+    per_wg = 2 if (m > 32 and tiles >= 512) else 1
+    rounds = -(-(-(-tiles // per_wg)) // 256)
+    t_one = 1500 * 1000 + rounds * k * (300 + 28 * m)
+    return t_split * 10000 < t_one * 2304
+
+
 def splitk_bytes_expected(m, n, k):
     """Split-K scratch size restated from its definition, for at least two whole
     128-wide chunks:
-    - 16 < m <= 64, or 5 <= m <= 16 with m k >= 8 * 28672: S = min(ceil(512 /
-      ceil(n / 128)), k // 128, 16) slices of whole chunks, split only if S >= 2
-      and 32 S m <= k;
-    - m > 64: S = min(256 // (ceil(m / 128) ceil(n / 256)), k // (8 m), k // 128,
-      16), split only if S >= 2;
+    - 5 <= m <= 64: S = min(ceil(512 / ceil(n / 128)), k // 128, 16); for
+      16 < m with 32 S m <= k that S, otherwise S cut to k // (32 m) and split
+      only if S >= 2 and the small-batch model favours it;
+    - m > 64: S = min(256 // (ceil(m / 128) ceil(n / 256)), cap, (k // 128) // 4,
+      16) with cap = k // (8 m), raised to (64 MiB) // (8 m n) where k >= 4096,
+      or k >= 2048 with at most 32 tiles; split only if S >= 2;
     one int32 [m, n] slice per slice of K actually used."""
     if m < 5 or k < 256:
         return 0
-    if m <= 16 and m * k < 8 * 28672:
-        return 0
+    nfull = k // 128
     if m > 64:
         tiles = -(-m // 128) * -(-n // 256)
-        s = min(256 // tiles, k // (8 * m), k // 128, 16)
+        cap = k // (8 * m)
+        if nfull >= 32 or (nfull >= 16 and tiles <= 32):
+            cap = max(cap, (64 << 20) // (8 * m * n))
+        s = min(256 // tiles, cap, nfull // 4, 16)
         if s < 2:
             return 0
     else:
-        ntb = -(-n // 128)
-        s = min(-(-512 // ntb), k // 128, 16)
-        if s < 2 or 32 * s * m > k:
+        s = min(-(-512 // -(-n // 128)), nfull, 16)
+        if not (m > 16 and 32 * s * m <= k):
+            s = min(s, k // (32 * m))
+            if s < 2 or not splitk_small_pays(m, n, k, s):
+                return 0
+        elif s < 2:
             return 0
-    kslice = -(-(k // 128) // s) * 128
+    kslice = -(-nfull // s) * 128
     return -(-k // kslice) * m * n * 4
 
 
@@ -190,17 +213,22 @@ def test_gemm_ws_workspace_and_validation(lib):
     assert ws(64, 8192, 28672) == 8 * 64 * 8192 * 4       # 8 slices of 28 chunks
     assert ws(20, 16384, 2624) == 5 * 20 * 16384 * 4      # 4 x 5 chunks + a half-chunk slice
     assert ws(17, 256, 10304) == 17 * 17 * 256 * 4        # 16 x 5 chunks + a half-chunk slice
-    assert ws(48, 8192, 8192) == 0                        # partials would outweigh the gain
+    assert ws(48, 8192, 8192) == 5 * 48 * 8192 * 4        # S cut from 8 to 5, modelled faster
+    assert ws(24, 4096, 4096) == 0                        # cut to 5 slices: one pass is faster
+    assert ws(64, 8192, 4096) == 0
     assert ws(16, 8192, 28672) == 8 * 16 * 8192 * 4       # a decode batch at large K
-    assert ws(16, 8192, 12288) == 0                       # m k below 8 * 28672
+    assert ws(16, 4096, 14336) == 0                       # one round of one-pass workgroups
+    assert ws(16, 1024, 28672) == 16 * 16 * 1024 * 4      # few channels leave CUs idle
     assert ws(4, 8192, 65536) == 0                        # m < 5 never splits
     assert ws(128, 8192, 28672) == 8 * 128 * 8192 * 4     # 32 tiles of 128 x 256: 8 slices
     assert ws(512, 8192, 28672) == 2 * 512 * 8192 * 4
+    assert ws(512, 4096, 4096) == 4 * 512 * 4096 * 4      # partials within 64 MiB
+    assert ws(512, 4096, 2048) == 0                       # k = 2048 with 64 tiles
+    assert ws(256, 2048, 2048) == 4 * 256 * 2048 * 4      # k = 2048 with 16 tiles
     assert ws(1024, 8192, 28672) == 0                     # 256 tiles fill the CUs
     assert ws(4096, 14336, 4096) == 0
-    assert ws(64, 8192, 4096) == 0
     # the rule over seeded random shapes around its edges (m range, half chunks,
-    # the 16-slice cap, the 32 S m <= k cut)
+    # the 16-slice cap, the 32 S m <= k cut, the modelled choice)
     rng = np.random.default_rng(7)
     for _ in range(2000):
         m = int(rng.integers(0, 80)) if rng.random() < 0.6 else int(rng.integers(64, 1100))

@@ -173,9 +173,9 @@ SPLITK_SHAPES = [
     (64, 28672, 8192),  # 70B-like FFN up shape, M = 64: 3 slices
     (17, 256, 10304),   # 16 slices of 5 chunks plus a 17th of the trailing half chunk
     (12, 8192, 28672),  # a decode batch below the 64-row tile: rows past m read zeros
-    (16, 4096, 14336),  # m k exactly at the small-batch threshold, 16 slices
-    (96, 8192, 4096),   # 128 x 256 tiles (m > 64), 5 slices, rows past m read zeros
-    (200, 2048, 16384), # 128 x 256 tiles, two row tiles (ragged), 10 slices
+    (16, 1024, 28672),  # a decode batch over few channels (CUs idle in one pass), 16 slices
+    (96, 8192, 4096),   # 128 x 256 tiles (m > 64), 8 slices, rows past m read zeros
+    (200, 2048, 16384), # 128 x 256 tiles, two row tiles (ragged), 16 slices
     (129, 4160, 8256),  # ragged M and N, 7 slices, the last ending on a half chunk
 ]
 
@@ -195,10 +195,10 @@ def test_gemm_splitk_int32_bit_exact(w4a8, m, n, k):
     assert np.array_equal(acc.cpu().numpy(), acc_ref)
 
 
-@pytest.mark.parametrize("m,n,k", SPLITK_SHAPES[:4] + [(48, 8192, 8192), (64, 48, 512)])
+@pytest.mark.parametrize("m,n,k", SPLITK_SHAPES[:4] + [(24, 4096, 4096), (64, 48, 512)])
 def test_gemm_splitk_equals_one_pass(w4a8, m, n, k):
-    # the last two are not split (partials would outweigh the gain; one column
-    # tile): w4a8_gemm_ws then takes the one-pass path
+    # the last two are not split (one pass is faster; one column tile):
+    # w4a8_gemm_ws then takes the one-pass path
     announce("gemm split-K vs one pass", m, n, k)
     _, dev_w, _ = _pack(w4a8, n, k, seed=5 * m + n)
     a = inputs.activations(m, k, seed=3 * m, outlier_frac=0.001)

@@ -40,14 +40,16 @@ def _compare(w4a8, a, packed, n, dt):
 
 @pytest.mark.parametrize("first,second", [
     ((64, 8192, 28672), (24, 14352, 4096)),   # split K both times (partials in the array)
-    ((300, 2048, 4096), (8, 4096, 4096)),     # tiled path, then the fused one-kernel path
-    ((2048, 512, 28672), (64, 512, 8192)),    # 56 MiB of codes, then a smaller tiled call
+    ((300, 2048, 1024), (8, 4096, 4096)),     # tiled path, then the fused one-kernel path
+    ((2048, 512, 28672), (64, 512, 8192)),    # 56 MiB of codes (no room for the partials:
+                                              # one pass), then a smaller split call
 ])
 def test_noalloc_equals_fused_with_workspace(w4a8, first, second):
+    if first == (2048, 512, 28672):
+        assert w4a8.workspace_bytes(2048, 28672, 512) > w4a8.NOALLOC_SCRATCH_BYTES
     for (m, n, k), seed in ((first, 3), (second, 5)):
         print("CASE noalloc", m, n, k, flush=True)
-        need = w4a8.workspace_bytes(m, k, n)
-        assert need <= w4a8.NOALLOC_SCRATCH_BYTES
+        assert w4a8.workspace_bytes(m, k) <= w4a8.NOALLOC_SCRATCH_BYTES
         a, packed = _case(w4a8, m, n, k, seed)
         for dt in (torch.int32, torch.bfloat16, torch.float32):
             _compare(w4a8, a, packed, n, dt)

@@ -266,7 +266,7 @@ def w4a8_gemm_ws(a_q, a_scale, w_packed, grp_scale, ch_scale, n: int,
                  out_dtype=torch.bfloat16, group: int = GROUP, out=None, workspace=None,
                  stream=None):
     """w4a8_gemm with a caller workspace that lets batches whose output tiles would
-    not fill the GPU (5 <= m <= 64 at large K, or m > 64 with few tiles) split K
+    not fill the GPU (5 <= m <= 64 where a split pays, or m > 64 with few tiles) split K
     (same result)."""
     _dev(a_q, torch.int8, "a_q")
     m, k = a_q.shape

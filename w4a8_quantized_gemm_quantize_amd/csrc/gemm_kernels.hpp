@@ -1266,43 +1266,70 @@ void launch_tiled_cols(const int8_t *a_q, const float *a_scale, const uint8_t *w
 // slice writing int32 partials, then a pass that sums the slices (exact, any
 // order) and applies the same binary32 epilogue as the one-pass kernels.
 constexpr int kSplitBM = 64, kSplitBN = 128;
-// Smallest m * k at which a batch of 5..16 rows splits.  Fused bf16 calls, n =
-// 8192, same boxes: m = 16, k = 28672 41.4 -> 33.6 us; m = 12 37.1 -> 31.8; m = 8
-// 32.9 -> 31.3; m = 16, k = 14336 26.5 -> 24.4; below it the split lost (m = 16,
-// k = 12288 21.7 -> 22.1; m = 8, k = 16384 21.8 -> 24.0; m = 5, k = 28672 29.8 ->
-// 30.7).
-constexpr int64_t kSplitSmallMK = 8 * 28672;
 // Batches of 65 rows and more whose 128 x 256 tiles number fewer than the
 // CUs: the one-pass kernels leave CUs idle (8192 x 28672, same box: m = 128 222
 // us, m = 256 182 us, against 36 us at m = 64 split), so K is split over
 // 128 x 256 tiles (the weights-in-registers form, one workgroup per CU).
 constexpr int kSplitMidBM = 128, kSplitMidBN = 256;
 constexpr int64_t kSplitMidWgs = 256;
+// Partials this small stay in the caches: more slices than twice the weight
+// bytes allow, for long enough K (A/B on MI355X, HIP events: 1024 x 8192 at
+// m = 768 58.0 -> 26.0 us, 5120 x 5120 at m = 384 41.8 -> 29.3, 4096 x 4096 at
+// m = 512 34.1 -> 27.2; at k = 2048 with 64 tiles or more the finalize pass
+// costs more than it saves: 8192 x 2048 at m = 384 22.2 -> 25.0).
+constexpr int64_t kSplitMidL2 = (int64_t)64 << 20;
+
+// Up to 64 rows, whether K is split at all comes from a model of the two
+// paths' times (ns, integers scaled to stay exact), fitted to MI355X
+// measurements of both over 46 shapes (m 5..64, n and k 1024..28672):
+//   one pass: 1500 + R k (300 + 28 m) / 1000, R = ceil(W / 256) rounds of its
+//             W workgroups (one 16-channel tile each; two for m > 32 and at
+//             least 512 tiles), each reading all of A through the vector
+//             memory path, which sets its pace;
+//   split:    7400 + 360 C max(256, G) / 256, C chunks per slice, G = S
+//             ceil(n / 128) workgroups (two finalizing launches' worth of
+//             fixed cost, then a chunk per 360 ns per CU);
+// K is split when the split model is below 0.9 of the one-pass model.  Over
+// the measured shapes the choice costs 0.5 % against the faster path of each
+// (the rule before it: 20 %); its worst pick is 13 % slower (48 x 13824 x 3072).
+inline bool splitk_small_pays(int64_t m, int64_t n, int64_t k, int64_t s) {
+    const int64_t ntb = (n + kSplitBN - 1) / kSplitBN;
+    const int64_t chunks = (k / kChunkK + s - 1) / s;
+    const int64_t wgs = ntb * s;
+    const __int128 t_split = (__int128)7400 * 256 + (__int128)360 * chunks * (wgs > 256 ? wgs : 256);
+    const int64_t ntiles = n / kNTile;
+    const int64_t per_wg = (m > 32 && ntiles >= 512) ? 2 : 1;
+    const int64_t rounds = ((ntiles + per_wg - 1) / per_wg + kSplitMidWgs - 1) / kSplitMidWgs;
+    const __int128 t_one = (__int128)1500 * 1000 + (__int128)rounds * k * (300 + 28 * m);
+    // t_split / 256 < 0.9 t_one / 1000
+    return t_split * 10000 < t_one * 2304;
+}
 
 // Slices of K for an m x n x k split-K product (0: not split).  Up to 64 rows
-// (16 < m <= 64, or 5 <= m <= 16 with m k >= kSplitSmallMK; the rows of a
-// 64-row tile past m cost MFMA work but no memory traffic): 64 x 128 tiles,
-// about 512 workgroups (two per CU: one alone leaves too few loads in flight),
-// at most 16 slices of at least one chunk.  The partials cost 8 S m n bytes
-// (written, then read) against n k / 2 bytes of 4-bit weights, so K is split
-// only while that stays within half the weights (32 S m <= k); below it the
-// one-pass kernel is faster (e.g. m = 48, n = k = 8192).  More rows: the
-// 128 x 256 form below.
+// (from 5; the rows of a 64-row tile past m cost MFMA work but no memory
+// traffic): 64 x 128 tiles, about 512 workgroups (two per CU: one alone leaves
+// too few loads in flight), at most 16 slices of at least one chunk.  The
+// partials cost 8 S m n bytes (written, then read) against n k / 2 bytes of
+// 4-bit weights: S is cut to keep them within half the weights (32 S m <= k).
+// For 16 < m with no cut, K is split; otherwise only where splitk_small_pays.
+// More rows: the 128 x 256 form.
 inline int64_t splitk_slices(int64_t m, int64_t n, int64_t k) {
     if (m < 5 || k < 2 * kChunkK) return 0;
-    if (m <= 16 && m * k < kSplitSmallMK) return 0;
     const int64_t nfull = k / kChunkK;
     if (m > 64) {
         // 128 x 256 tiles with weights in registers (one workgroup per CU):
         // split while the tiles alone would leave CUs idle, into at most one
         // round of kSplitMidWgs workgroups, with the partials within twice
-        // the weight bytes (8 S m n <= n k): idle CUs cost more than that
-        // traffic at these sizes
+        // the weight bytes (8 S m n <= n k) or kSplitMidL2 (k >= 4096, or
+        // k >= 2048 with at most 32 tiles), slices of at least 4 chunks
         const int64_t tiles = ((m + kSplitMidBM - 1) / kSplitMidBM) *
                               ((n + kSplitMidBN - 1) / kSplitMidBN);
         int64_t s = kSplitMidWgs / tiles;
-        if (s > k / (8 * m)) s = k / (8 * m);
-        if (s > nfull) s = nfull;
+        int64_t cap = k / (8 * m);
+        if ((nfull >= 32 || (nfull >= 16 && tiles <= 32)) && cap < kSplitMidL2 / (8 * m * n))
+            cap = kSplitMidL2 / (8 * m * n);
+        if (s > cap) s = cap;
+        if (s > nfull / 4) s = nfull / 4;
         if (s > 16) s = 16;
         return s >= 2 ? s : 0;
     }
@@ -1310,8 +1337,10 @@ inline int64_t splitk_slices(int64_t m, int64_t n, int64_t k) {
     int64_t s = (512 + ntb - 1) / ntb;
     if (s > nfull) s = nfull;
     if (s > 16) s = 16;
-    if (s < 2 || 32 * s * m > k) return 0;
-    return s;
+    if (m > 16 && 32 * s * m <= k) return s >= 2 ? s : 0;
+    if (s > k / (32 * m)) s = k / (32 * m);
+    if (s < 2) return 0;
+    return splitk_small_pays(m, n, k, s) ? s : 0;
 }
 inline int64_t splitk_kslice(int64_t k, int64_t s) {
     const int64_t nfull = k / kChunkK;

@@ -23,7 +23,7 @@ hipError_t launch_unpack_w4(const uint8_t *w_packed, const uint8_t *grp_scale, i
 // partials (optional, splitk_partial_bytes(m, n, k) bytes, 16-byte aligned):
 // int32 scratch that lets batches whose output tiles would not fill the GPU
 // split K over workgroups (splitk_slices); without it those
-// shapes run the one-pass skinny kernel.  Same result bit for bit either way.
+// shapes run the one-pass kernels.  Same result bit for bit either way.
 size_t splitk_partial_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_w4a8_gemm(const int8_t *a_q, const float *a_scale, const uint8_t *w_packed,
                             const uint8_t *grp_scale, const float *ch_scale, int64_t m,

@@ -55,8 +55,11 @@ w4a8_status w4a8_gemm_bf16act_noalloc(const uint16_t *a, const uint8_t *w_packed
     if (k <= 0 || m < 0 || n < 0) return W4A8_ERR_SHAPE;
     if (m == 0 || n == 0) return W4A8_OK;
     const size_t base = w4a8_gemm_bf16act_workspace_bytes(m, k);
-    const size_t need = base + w4a8_gemm_workspace_bytes(m, n, k);
-    if (base == 0 || need > (size_t)W4A8_NOALLOC_SCRATCH_BYTES) return W4A8_ERR_UNSUPPORTED;
+    if (base == 0 || base > (size_t)W4A8_NOALLOC_SCRATCH_BYTES) return W4A8_ERR_UNSUPPORTED;
+    // the split-K partials only when they fit beside the codes; otherwise the
+    // one-pass kernels, whose result is the same bit for bit
+    size_t need = base + w4a8_gemm_workspace_bytes(m, n, k);
+    if (need > (size_t)W4A8_NOALLOC_SCRATCH_BYTES) need = base;
     if (!a || !w_packed || !grp_scale || !ch_scale || !out) return W4A8_ERR_NULL;
     if (!aligned16(a) || !aligned16(w_packed) || !aligned16(grp_scale) || !aligned16(ch_scale) ||
         !aligned16(out))
