@@ -504,32 +504,35 @@ def main():
 
 def quantizer_leg(torch, w4a8, inputs, dev, stream, reps=20):
     """Standalone quantizer workload: 64M bf16 ~ N(0,1) as [65536, 1024], blocks 32
-    and 128.  Two input/output sets alternate (2 x 200 MB) so reads come from HBM."""
+    and 128.  Input/output sets of ~200 MB rotate, more than 512 MB in all, so
+    reads come from HBM (not the 256 MB last-level cache)."""
     spec = inputs.QUANTIZER
     rows, cols = spec["rows"], spec["cols"]
     x0 = torch.from_numpy(inputs.activations(rows, cols, seed=0).view(np.int16)) \
         .view(torch.bfloat16).to(dev)
-    xs = [x0, x0.clone()]
-    res = {"workload": f"{rows}x{cols} bf16 ~ N(0,1) (64M elements, seed 0)"}
+    ncp = n_copies(rows * cols * 3 + 4 * (rows * cols // 32))
+    xs = [x0] + [x0.clone() for _ in range(ncp - 1)]
+    res = {"workload": f"{rows}x{cols} bf16 ~ N(0,1) (64M elements, seed 0), "
+                       f"{ncp} buffer sets rotated"}
     for block in spec["blocks"]:
-        qs = [torch.empty((rows, cols), dtype=torch.int8, device=dev) for _ in range(2)]
+        qs = [torch.empty((rows, cols), dtype=torch.int8, device=dev) for _ in range(ncp)]
         ss = [torch.empty((rows, cols // block), dtype=torch.float32, device=dev)
-              for _ in range(2)]
+              for _ in range(ncp)]
         def quant(r, st, block=block, qs=qs, ss=ss):
             w4a8.quantize_act_blockwise(xs[r], block, q=qs[r], scales=ss[r], stream=st)
-        # graph replays of the two input/output sets in turn, as for the GEMMs
+        # graph replays of the input/output sets in turn, as for the GEMMs
         # (per-call events would add the launch gaps to a 35-40 us kernel)
-        ms = time_graph(torch, quant, 2, reps // 4)
+        ms = time_graph(torch, quant, ncp, reps)
         gbps = quantizer_algorithmic_bytes(rows * cols, block) / (ms * 1e-3) / 1e9
         entry = {"kernel_ms": ms, "achieved": gbps, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS}
         # dequantization round trip: q, scales -> fp32 and bf16; MSE against x
         elems = rows * cols
         for name, dt, ob in (("dequant_f32", torch.float32, 4), ("dequant_bf16", torch.bfloat16, 2)):
-            outs = [torch.empty((rows, cols), dtype=dt, device=dev) for _ in range(2)]
+            outs = [torch.empty((rows, cols), dtype=dt, device=dev) for _ in range(ncp)]
 
             def deq(r, st, outs=outs, dt=dt):
                 w4a8.dequantize_act_blockwise(qs[r], ss[r], block, dt, out=outs[r], stream=st)
-            dms = time_graph(torch, deq, 2, 10)
+            dms = time_graph(torch, deq, ncp, 10)
             dbytes = elems * (1 + ob) + 4 * (elems // block)
             x64 = xs[0].double()
             mse = float(((outs[0].double() - x64) ** 2).mean())
