@@ -108,12 +108,19 @@ def fused_form(m, n, k, ncu):
     vectors per thread)."""
     if m < 1 or m > 16 or k < 128 or m * (k + 16) > 48 * 1024:
         return None
-    waves = 16 if k <= 8192 else 8
-    tpr = 64 * waves
-    while tpr * m > 64 * waves:
-        tpr //= 2
-    need = -(-(k // 8) // tpr)
-    av = 4 if need <= 4 else 8 if need <= 8 else None
+
+    def need(waves):
+        tpr = 64 * waves
+        while tpr * m > 64 * waves:
+            tpr //= 2
+        return -(-(k // 8) // tpr)
+    # 8 wavefronts for k > 2048, unless they would need more than 8 vectors per
+    # thread, or more than 4 with at most one workgroup per CU
+    if k <= 2048 or need(8) > 8 or (need(8) > 4 and n // 16 <= ncu):
+        waves = 16
+    else:
+        waves = 8
+    av = 4 if need(waves) <= 4 else 8 if need(waves) <= 8 else None
     if av is None:
         return None
     keep = av == 4 and waves == 16 and n // 16 <= ncu
@@ -122,10 +129,11 @@ def fused_form(m, n, k, ncu):
 
 FUSED_FORMS = [
     ((8, 4096, 4096), (4, 16, True)),     # decode: one workgroup per CU
-    ((8, 8192, 4096), (4, 16, False)),    # more workgroups than CUs
-    ((16, 64, 2560), (8, 16, False)),
+    ((4, 8192, 2048), (4, 16, False)),    # short rows, more workgroups than CUs
+    ((16, 64, 2560), (8, 16, False)),     # 8 wavefronts would need 10 vectors
     ((1, 64, 12288), (4, 8, False)),
-    ((1, 512, 28672), (8, 8, False)),     # FFN-down M = 1 row length
+    ((8, 8192, 4096), (8, 8, False)),     # more workgroups than CUs
+    ((1, 512, 28672), (4, 16, True)),     # FFN-down M = 1 row length, few channels
     ((3, 48, 8192), (4, 16, True)),
 ]
 

@@ -128,12 +128,32 @@ __device__ __forceinline__ u32x4 buffer_load16_nt(__amdgpu_buffer_rsrc_t r, int 
 
 // ---------------------------------------------------------------- skinny --
 constexpr int kSkinnyMaxVec = 8;    // fused prologue: 16-byte vectors held per thread
-// Wavefronts per workgroup of the fused form: 16 when the weight stream per
-// workgroup is short (the quantization prologue, which every workgroup runs over
-// all of A, then dominates and gets four wavefronts per SIMD), else 8 with
-// deeper load batches for the long stream.
-constexpr int64_t kFusedShortK = 8192;
-inline int fused_waves(int64_t k) { return k <= kFusedShortK ? 16 : 8; }
+// Row vectors (8 activations each) per thread of the fused prologue with
+// `waves` wavefronts: the rows split over threads in power-of-two groups.
+inline int64_t fused_need(int64_t m, int64_t k, int waves) {
+    const int64_t threads = 64 * waves;
+    int64_t tpr = threads;
+    while (tpr * m > threads) tpr >>= 1;
+    return (k / 8 + tpr - 1) / tpr;
+}
+// Wavefronts per workgroup of the fused form.  8, with deeper load batches,
+// once each wavefront's share of the weight stream is long enough (k > 2048);
+// 16 for short rows (the prologue, which every workgroup runs over all of A,
+// then dominates and gets four wavefronts per SIMD), when 8 wavefronts would
+// need more than kSkinnyMaxVec vectors per thread, and when the workgroups
+// fit one per CU with more than four vectors per thread (8 x 4096 x 4096:
+// 6.50 us with 16, 6.86 with 8).  A/B on MI355X, fused calls, 16 -> 8
+// wavefronts: 1 x 28672 x 4096 21.3 -> 15.9 us, 1 x 28672 x 8192 29.8 ->
+// 24.8, 2 x 14336 x 4096 12.9 -> 10.4, 1 x 8192 x 8192 10.6 -> 9.7; at k =
+// 2048 no difference.
+constexpr int64_t kFusedShortK = 2048;
+inline int fused_waves(int64_t m, int64_t n, int64_t k, int64_t ncu) {
+    if (k <= kFusedShortK) return 16;
+    const int64_t need8 = fused_need(m, k, 8);
+    if (need8 > kSkinnyMaxVec) return 16;
+    if (need8 > 4 && n / kNTile <= ncu) return 16;
+    return 8;
+}
 
 template <int WF, int NT, int D, int MT, bool WITH_ACT, int AB>
 struct WeightBatch {
@@ -1476,13 +1496,10 @@ constexpr int64_t kFusedLdsMax = 48 * 1024;
 
 // Activation vectors per thread the fused prologue needs for m rows of k
 // (0 if the fused form does not apply).
-[[maybe_unused]] int fused_vectors(int64_t m, int64_t k) {
+[[maybe_unused]] int fused_vectors(int64_t m, int64_t n, int64_t k, int64_t ncu) {
     if (m < 1 || m > 16 || k < kChunkK) return 0;
     if (m * (k + 16) > kFusedLdsMax) return 0;
-    const int64_t threads = 64 * fused_waves(k);
-    int64_t tpr = threads;
-    while (tpr * m > threads) tpr >>= 1;
-    const int64_t need = (k / 8 + tpr - 1) / tpr;
+    const int64_t need = fused_need(m, k, fused_waves(m, n, k, ncu));
     return need <= 4 ? 4 : need <= kSkinnyMaxVec ? 8 : 0;
 }
 
@@ -1534,11 +1551,11 @@ hipError_t launch_gemm_bf16act_fmt(const uint16_t *a, const uint8_t *w_packed,
                                     int8_t *ws_q, float *ws_s, hipStream_t stream,
                                     int32_t *partials = nullptr) {
     if (m == 0 || n == 0) return hipSuccess;
-    const int av = fused_vectors(m, k);
+    const int ncu = device_cu_count();
+    const int av = fused_vectors(m, n, k, ncu);
     if (av > 0) {
         const size_t lds_bytes = (size_t)(m * (k + 16));
-        const bool w16 = fused_waves(k) == 16;
-        const int ncu = device_cu_count();
+        const bool w16 = fused_waves(m, n, k, ncu) == 16;
         // one workgroup per 16-channel tile: at most one per CU -> keep the floats
         const bool one_per_cu = n / kNTile <= (int64_t)ncu;
         if (av == 4 && w16 && one_per_cu)
