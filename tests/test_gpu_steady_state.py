@@ -103,9 +103,9 @@ def test_tiled_256_steady_state(w4a8, m, n, k, fmt):
 
 def fused_form(m, n, k, ncu):
     """The launcher's form of the fused kernel: (vectors per thread, wavefronts,
-    widened activations kept in registers), or None when the shape runs
-    quantize then GEMM (m > 16, activations past 48 KB of LDS, or more than 8
-    vectors per thread)."""
+    widened activations kept in registers, 16-channel tiles per workgroup), or
+    None when the shape runs quantize then GEMM (m > 16, activations past 48 KB
+    of LDS, or more than 8 vectors per thread)."""
     if m < 1 or m > 16 or k < 128 or m * (k + 16) > 48 * 1024:
         return None
 
@@ -124,17 +124,21 @@ def fused_form(m, n, k, ncu):
     if av is None:
         return None
     keep = av == 4 and waves == 16 and n // 16 <= ncu
-    return av, waves, keep
+    # two tiles per workgroup: 4 vectors, 8 wavefronts, more than two
+    # workgroups per CU, at least 8192 activations per workgroup
+    tiles = 2 if av == 4 and waves == 8 and n // 16 > 2 * ncu and m * k >= 8192 else 1
+    return av, waves, keep, tiles
 
 
 FUSED_FORMS = [
-    ((8, 4096, 4096), (4, 16, True)),     # decode: one workgroup per CU
-    ((4, 8192, 2048), (4, 16, False)),    # short rows, more workgroups than CUs
-    ((16, 64, 2560), (8, 16, False)),     # 8 wavefronts would need 10 vectors
-    ((1, 64, 12288), (4, 8, False)),
-    ((8, 8192, 4096), (8, 8, False)),     # more workgroups than CUs
-    ((1, 512, 28672), (4, 16, True)),     # FFN-down M = 1 row length, few channels
-    ((3, 48, 8192), (4, 16, True)),
+    ((8, 4096, 4096), (4, 16, True, 1)),     # decode: one workgroup per CU
+    ((4, 8192, 2048), (4, 16, False, 1)),    # short rows, more workgroups than CUs
+    ((16, 64, 2560), (8, 16, False, 1)),     # 8 wavefronts would need 10 vectors
+    ((1, 64, 12288), (4, 8, False, 1)),
+    ((8, 8192, 4096), (8, 8, False, 1)),     # more workgroups than CUs
+    ((1, 512, 28672), (4, 16, True, 1)),     # FFN-down M = 1 row length, few channels
+    ((3, 48, 8192), (4, 16, True, 1)),
+    ((2, 14352, 4096), (4, 8, False, 2)),    # two tiles per workgroup, the last one alone
 ]
 
 

@@ -154,6 +154,16 @@ inline int fused_waves(int64_t m, int64_t n, int64_t k, int64_t ncu) {
     if (need8 > 4 && n / kNTile <= ncu) return 16;
     return 8;
 }
+// The 8-wavefront form with 4 vectors per thread takes two 16-channel tiles
+// per workgroup (load batches of two chunks) when the grid would have more
+// than two workgroups per CU and each converts at least 8192 activations:
+// half the workgroups then repeat the conversion of A (A/B on MI355X, fused
+// calls: 2 x 14336 x 4096 10.9 -> 9.8 us, 1 x 14336 x 8192 14.8 -> 13.4,
+// 4 x 28672 x 4096 19.8 -> 18.6, 1 x 28672 x 8192 26.3 -> 24.8; with 4096
+// activations no gain: 1 x 28672 x 4096 16.6 -> 16.8).
+inline bool fused_two_tiles(int64_t m, int64_t n, int64_t k, int64_t ncu) {
+    return n / kNTile > 2 * ncu && m * k >= 8192;
+}
 
 template <int WF, int NT, int D, int MT, bool WITH_ACT, int AB>
 struct WeightBatch {
@@ -1242,7 +1252,7 @@ void launch_skinny(const void *act, const float *a_scale, const uint8_t *w_packe
     // tiles.  The fused form runs 16 wavefronts so its quantization prologue
     // (every workgroup converts all of A) has four wavefronts per SIMD.
     constexpr int WAVES = FUSED ? FW : 8,
-                  D = FUSED ? (FW == 16 ? 2 : 4)
+                  D = FUSED ? (FW == 16 || NT == 2 ? 2 : 4)
                             : (MT == 1 ? 4 : (MT == 2 ? 2 : (NT == 1 && AB == 0 ? 2 : 1)));
     const int64_t ntiles = n / kNTile;
     const unsigned grid = (unsigned)((ntiles + NT - 1) / NT);
@@ -1570,6 +1580,9 @@ hipError_t launch_gemm_bf16act_fmt(const uint16_t *a, const uint8_t *w_packed,
             launch_skinny<WF, 1, 1, true, 8, 0, 16>(a, nullptr, w_packed, grp_scale, ch_scale, m,
                                                     n, k, out, out_dtype, ws_q, ws_s, lds_bytes,
                                                     stream);
+        else if (av == 4 && fused_two_tiles(m, n, k, ncu))
+            launch_skinny<WF, 1, 2, true, 4, 0, 8>(a, nullptr, w_packed, grp_scale, ch_scale, m, n,
+                                                   k, out, out_dtype, ws_q, ws_s, lds_bytes, stream);
         else if (av == 4)
             launch_skinny<WF, 1, 1, true, 4, 0, 8>(a, nullptr, w_packed, grp_scale, ch_scale, m, n,
                                                    k, out, out_dtype, ws_q, ws_s, lds_bytes, stream);
