@@ -214,6 +214,41 @@ def test_gemm_splitk_equals_one_pass(w4a8, m, n, k):
                            y2.view(torch.int32) if dt != torch.bfloat16 else y2.view(torch.int16))
 
 
+# Shapes the split rules send to split K, across their branches: the small-batch
+# cost model (m <= 16, and 16 < m <= 64 with the slice count cut to k / 32m),
+# few output channels, and m > 64 with partials up to 64 MiB.  The one-pass
+# kernels are compared with the oracle element by element elsewhere; here the
+# split result must equal theirs bit for bit in every output type.
+MODEL_SPLIT_SHAPES = [
+    (8, 28672, 8192), (16, 5120, 14336), (12, 11008, 13824), (5, 28672, 28672),
+    (16, 28672, 4096), (48, 1024, 8192), (64, 2048, 8192), (32, 14336, 4096),
+    (40, 4160, 11008), (100, 1040, 6144), (256, 2048, 2048), (192, 4096, 4096),
+    (384, 5120, 5120), (768, 1024, 8192),
+]
+
+
+@pytest.mark.parametrize("m,n,k", MODEL_SPLIT_SHAPES)
+def test_model_split_shapes_equal_one_pass(w4a8, m, n, k):
+    announce("split rule shape vs one pass", m, n, k)
+    need = w4a8.gemm_workspace_bytes(m, n, k)
+    assert need > 0
+    # weights drawn on the device (seeded): no oracle is needed for this comparison
+    g = torch.Generator(device="cuda").manual_seed(m + n + k)
+    w = (torch.randn((n, k), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    dev_w = w4a8.pack_w4_grouped(w)
+    del w
+    a = inputs.activations(m, k, seed=7 * m + 1, outlier_frac=0.001)
+    q, s = w4a8.quantize_act_blockwise(to_dev_bf16(a), k)
+    s = s.reshape(-1)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for dt in (torch.int32, torch.bfloat16, torch.float32):
+        y1 = w4a8.w4a8_gemm(q, s, *dev_w, n, out_dtype=dt)
+        y2 = w4a8.w4a8_gemm_ws(q, s, *dev_w, n, out_dtype=dt, workspace=ws)
+        torch.cuda.synchronize()
+        view = torch.int16 if dt == torch.bfloat16 else torch.int32
+        assert torch.equal(y1.view(view), y2.view(view)), dt
+
+
 @pytest.mark.parametrize("m,n,k", [(24, 14352, 4096), (16, 8192, 14336)])
 @pytest.mark.parametrize("fmt", ["w4", "lqq", "w8"])
 def test_fused_splitk_workspace_equals_without(w4a8, fmt, m, n, k):
