@@ -1249,8 +1249,10 @@ void launch_skinny(const void *act, const float *a_scale, const uint8_t *w_packe
                    int64_t k, void *out, int out_dtype, int8_t *ws_q, float *ws_s,
                    size_t dyn_lds, hipStream_t stream) {
     // chunks per load batch: fewer when each batch also carries MT activation
-    // tiles.  The fused form runs 16 wavefronts so its quantization prologue
-    // (every workgroup converts all of A) has four wavefronts per SIMD.
+    // tiles.  The fused form runs FW wavefronts (fused_waves: 16 give its
+    // quantization prologue, which every workgroup runs over all of A, four
+    // wavefronts per SIMD; 8 take deeper batches of the weight stream), and
+    // with two tiles per workgroup batches of two chunks.
     constexpr int WAVES = FUSED ? FW : 8,
                   D = FUSED ? (FW == 16 || NT == 2 ? 2 : 4)
                             : (MT == 1 ? 4 : (MT == 2 ? 2 : (NT == 1 && AB == 0 ? 2 : 1)));
@@ -1317,8 +1319,9 @@ constexpr int64_t kSplitMidL2 = (int64_t)64 << 20;
 //             least 512 tiles), each reading all of A through the vector
 //             memory path, which sets its pace;
 //   split:    7400 + 360 C max(256, G) / 256, C chunks per slice, G = S
-//             ceil(n / 128) workgroups (two finalizing launches' worth of
-//             fixed cost, then a chunk per 360 ns per CU);
+//             ceil(n / 128) workgroups (a fixed cost for the two launches,
+//             the sliced kernel and the sum pass, and the pipeline fill;
+//             then a chunk per 360 ns per CU);
 // K is split when the split model is below 0.9 of the one-pass model.  Over
 // the measured shapes the choice costs 0.5 % against the faster path of each
 // (the rule before it: 20 %); its worst pick is 13 % slower (48 x 13824 x 3072).
