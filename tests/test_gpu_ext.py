@@ -92,7 +92,9 @@ def test_lqq_gemm_int32_bit_exact(w4a8, m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(16, 256, 256), (5, 48, 192), (200, 272, 384),
-                                   (8, 4096, 4096)])
+                                   (8, 4096, 4096),
+                                   (1, 8192, 4096),     # fused: 8 wavefronts, one tile each
+                                   (2, 14352, 4096)])   # fused: two tiles per workgroup
 def test_lqq_gemm_float_outputs_and_fused(w4a8, m, n, k):
     announce("lqq gemm f32/bf16 + fused", m, n, k)
     dev_w, ref_w = _lqq_pack(w4a8, n, k, seed=3 * m + n)
@@ -167,7 +169,9 @@ def test_w8a8_gemm_int32_bit_exact(w4a8, m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(16, 256, 256), (5, 48, 192), (200, 272, 384),
-                                   (8, 4096, 4096)])
+                                   (8, 4096, 4096),
+                                   (1, 8192, 4096),     # fused: 8 wavefronts, one tile each
+                                   (2, 14352, 4096)])   # fused: two tiles per workgroup
 def test_w8a8_float_outputs_and_fused(w4a8, m, n, k):
     announce("w8a8 f32/bf16 + fused", m, n, k)
     w = edge_weights(n, k, seed=m + 3 * n)
