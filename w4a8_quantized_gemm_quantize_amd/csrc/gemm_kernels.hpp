@@ -326,7 +326,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
         }
         // The first weight batch is requested after the activations: loads
         // complete in order, so waiting for the activations below does not wait
-        // for the weights, which stream in while the prologue runs.
+        // for the weights, which stream in while the prologue runs.  The
+        // scheduling barrier keeps every activation load ahead of the weight
+        // requests: the compiler had moved the last two of eight after the
+        // group-parameter loads, and the row maximum then waited for those.
+        __builtin_amdgcn_sched_barrier(0);
         load_batch(cur, j0);
         lds_barrier();  // red / amax_lds cleared
         // With KF each vector is widened once and the floats are kept for the
