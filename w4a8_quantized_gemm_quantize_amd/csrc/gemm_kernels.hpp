@@ -205,9 +205,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     const int c = lane & 15, kq = lane >> 4;
     const int64_t ntiles = n / kNTile;
     const int64_t t0 = (int64_t)blockIdx.x * NT;
-    const int64_t nchunks = (k + kChunkK - 1) / kChunkK;
-    const int64_t G = k / kGroup;
-    const int64_t lds_stride = k + 16;
+    // k <= K_MAX: the K-derived counts fit 32 bits (shorter scalar code ahead
+    // of the first loads: 150 -> 123 instructions before the decode kernel's
+    // last prologue request, decode 6.52 -> 6.46 us, 4 x 4096 x 4096 5.67 ->
+    // 5.52 us on one box)
+    const int k32 = (int)k;
+    const int nchunks = (k32 + kChunkK - 1) >> 7;
+    const int G = k32 >> 6;
+    const int lds_stride = k32 + 16;
 
     if constexpr (AB == 0)
         for (int i = tid; i < NT * 16 * (ROWS + 4); i += THREADS) (&red[0][0][0])[i] = 0;
@@ -220,11 +225,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     // only use this kernel for k >= 128 (at least one full chunk), so a
     // wavefront without chunks of its own (j0 >= j1) still loads a valid one,
     // chunk j1 - 1 = nfull - 1, and never uses it.
-    const int64_t nfull = k / kChunkK;
+    const int nfull = k32 >> 7;
     const bool has_half = nfull < nchunks;
-    const int per = (int)((nfull + WAVES - 1) / WAVES);
+    const int per = (nfull + WAVES - 1) / WAVES;
     const int j0 = wave * per;
-    const int j1 = (j0 + per < (int)nfull) ? j0 + per : (int)nfull;
+    const int j1 = (j0 + per < nfull) ? j0 + per : nfull;
     const int8_t *a_q = (const int8_t *)act;
 
     // Buffer resources over this workgroup's weight tiles and their group
@@ -245,7 +250,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
         buffer_rsrc(w_packed + t0 * (int64_t)wtile, (uint32_t)tiles_here * wtile);
     const __amdgpu_buffer_rsrc_t rp =
         WF == kW8 ? rw : buffer_rsrc(grp_scale + t0 * (int64_t)ptile, (uint32_t)tiles_here * ptile);
-    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(act, FUSED ? 16u : (uint32_t)(m * k));
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(act, FUSED ? (uint32_t)(m * k32 * 2) : (uint32_t)(m * k));
     const WParamSel psel = wparam_selectors<WF>(c);
     const int poff_c = WF == kW4Lqq ? (c & ~1) * 2 : (c & ~3);
     int aoff[FUSED ? 1 : MT];                    // activation row offsets (rows past m: row m - 1)
@@ -309,20 +314,19 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
         // Per-row absmax -> scale, then the row's codes into LDS.  Threads are
         // split into m groups of tpr (a power of two) threads per row.  All
         // loads are issued before any is used.
-        const u32x4 *a16 = (const u32x4 *)act;
-        const int64_t vpr = k / 8;
+        const int vpr = k32 >> 3;
         int tpr = THREADS;
         while (tpr * m > THREADS) tpr >>= 1;
         const int row = tid / tpr, sub = tid % tpr;
         const bool row_ok = row < m;
         // Unconditional loads from clamped (valid) addresses; vectors outside the
-        // row are ignored below.
-        const int64_t rowc = row_ok ? row : m - 1;
+        // row are ignored below.  32-bit buffer offsets (m k <= 16 K_MAX).
+        const int rowbase = (row_ok ? row : m - 1) * vpr;
         u32x4 av[AV];
 #pragma unroll
         for (int u = 0; u < AV; ++u) {
-            const int64_t v = sub + (int64_t)u * tpr;
-            av[u] = a16[rowc * vpr + (v < vpr ? v : vpr - 1)];
+            const int v = sub + u * tpr;
+            av[u] = buffer_load16(ra, (rowbase + (v < vpr ? v : vpr - 1)) * 16, 0);
         }
         // The first weight batch is requested after the activations: loads
         // complete in order, so waiting for the activations below does not wait
