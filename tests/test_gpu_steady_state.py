@@ -139,6 +139,8 @@ FUSED_FORMS = [
     ((1, 512, 28672), (4, 16, True, 1)),     # FFN-down M = 1 row length, few channels
     ((3, 48, 8192), (4, 16, True, 1)),
     ((2, 14352, 4096), (4, 8, False, 2)),    # two tiles per workgroup, the last one alone
+    ((2, 4096, 4160), (4, 8, False, 1)),     # 8 wavefronts with a trailing 64-wide chunk
+    ((2, 14352, 4160), (4, 8, False, 2)),    # two tiles and a trailing 64-wide chunk
 ]
 
 
